@@ -1,0 +1,83 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/w8a8.h declares, and rejects bad arguments on the host (before any
+device work) with the documented status codes."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import w8a8_fp8_linear_amd as w8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
+
+OK, NULL, SHAPE, MIS, UNSUP, WS, DEV, LAUNCH = range(8)
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        names |= set(DECL.findall(open(h).read()))
+    return names
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    assert {"quantize_per_token", "w8a8_gemm", "w8a8_abi_version", "w8a8_status_string"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(w8.lib_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    assert _declared() <= set(w8._SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    assert w8.abi_version() == 1
+    for s in range(8):
+        assert w8.lib().w8a8_status_string(s)
+    assert w8.lib().w8a8_status_string(99) == b"unknown status"
+
+
+P = 1 << 20   # a fake, 16-byte aligned address; never dereferenced (checks fail first)
+
+
+def test_quantize_argument_errors():
+    f = w8.lib().quantize_per_token
+    assert f(P, -1, 16, P, P, None) == SHAPE
+    assert f(P, 4, -16, P, P, None) == SHAPE
+    assert f(P, 1 << 62, 1 << 4, P, P, None) == SHAPE
+    assert f(P, 4, 0, P, P, None) == UNSUP
+    assert f(P, 4, 24, P, P, None) == UNSUP
+    assert f(P, 0, 16, P, P, None) == OK          # empty: no-op, no device needed
+    assert f(None, 4, 16, P, P, None) == NULL
+    assert f(P, 4, 16, None, P, None) == NULL
+    assert f(P, 4, 16, P, None, None) == NULL
+    assert f(P + 8, 4, 16, P, P, None) == MIS
+    assert f(P, 4, 16, P + 4, P, None) == MIS
+
+
+def test_gemm_argument_errors():
+    f = w8.lib().w8a8_gemm
+    assert f(P, P, P, P, P, -1, 16, 16, None) == SHAPE
+    assert f(P, P, P, P, P, 4, 16, 8, None) == UNSUP
+    assert f(P, P, P, P, P, 4, 24, 16, None) == UNSUP
+    assert f(P, P, P, P, P, 0, 16, 16, None) == OK
+    assert f(P, P, P, P, P, 4, 0, 16, None) == OK
+    assert f(None, P, P, P, P, 4, 16, 16, None) == NULL
+    assert f(P, P, P, P, None, 4, 16, 16, None) == NULL
+    assert f(P, P, P + 1, P, P, 4, 16, 16, None) == MIS
+
+
+def test_valid_call_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert w8.lib().quantize_per_token(P, 4, 16, P, P, None) == DEV
+    assert w8.lib().w8a8_gemm(P, P, P, P, P, 4, 16, 16, None) == DEV

@@ -1,0 +1,96 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+//
+// Formats: activations and outputs are BF16 (the model's dtype; Lernex/
+// Metis-1.6-Logos-FP8, "What --fast-math does"), FP8 is OCP E4M3FN (the
+// F8_E4M3 tensor type of the checkpoints; Lernex/Metis-1.6-Praxis-NVFP4, hub
+// sidebar), scales are float32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource word 3 for raw (untyped) buffers on gfx9-class parts.
+constexpr int kBufferFlags = 0x00020000;
+// Any voffset at or above this is outside every resource built by make_rsrc,
+// so the hardware returns zeros for the load.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Raw buffer resource over [base, base + bytes); bytes is clamped so that
+// kOutOfRange always lies outside it.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7FFFFFF0ll) bytes = 0x7FFFFFF0ll;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+__device__ inline v4i buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes lds_base + 16 * i (lds_base must be wave-uniform).
+__device__ inline void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// FP8 x FP8 -> FP32 matrix-core step, 16x16 outputs, 128-deep. cbsz/blgp 0
+// select E4M3 for both operands; zero scale operands select the unscaled
+// instruction.
+__device__ inline v4f mfma_16x16x128_e4m3(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// float32 -> BF16 bits, round to nearest even (finite inputs).
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> E4M3FN code: round to nearest, ties to even, |v| >= 448
+// saturates to 448, the sign bit is kept on a zero result. Written on the
+// float32 bit fields; NaN (out of contract) saturates.
+__device__ inline uint32_t e4m3_rne_sat(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                 // |v| >= 448
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {          // 2^-6 <= |v| < 448: normal E4M3
+    const uint32_t rest = a & 0xFFFFFu;
+    code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+    code += (rest > 0x80000u) | ((rest == 0x80000u) & (code & 1u));
+  } else {                                // multiple of 2^-9, scaling by 512 is exact
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return code | sign;
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ inline float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace w8a8

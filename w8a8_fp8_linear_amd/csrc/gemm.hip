@@ -1,0 +1,281 @@
+// Scaled FP8 GEMM: Y[m, n] = bf16( sa[m] * sw[n] * sum_k dec(A[m, k]) * dec(W[n, k]) ).
+//
+// This is the multiply the pages' fast-math path performs: each layer's
+// input rounded to FP8 per token and multiplied with the FP8 weights on the
+// FP8 matrix units (Lernex/Metis-1.6-Logos-FP8, "What --fast-math does"),
+// weights stored [out, in] with one scale per output row (Lernex/Metis-1.6-
+// Praxis-NVFP4, "What is in NVFP4"). Both operands are K-contiguous.
+//
+// Two kernels:
+//  * gemm_tiled: many tokens (prompt reading). A workgroup of 4 waves owns a
+//    BM x BN output tile. Each 128-deep K step of both operand tiles is
+//    copied global -> LDS by buffer loads that write LDS directly (no VGPR
+//    staging), double-buffered; each wave then runs 16x16x128 E4M3 MFMAs on
+//    a (BM/2) x (BN/2) sub-tile with fp32 accumulators. The epilogue applies
+//    both scales in fp32, rounds to BF16 and goes through LDS so that every
+//    global store is a full 16-byte row segment. Workgroup ids are renumbered
+//    so that each of the 8 XCDs walks a compact block of tiles (its own L2).
+//  * gemm_skinny: at most 32 tokens (decode). The time is the weight stream
+//    (the pages: that step is set by how fast the GPU reads the weights;
+//    "What --fast-math does"). A workgroup owns 16 weight rows, its 4 waves
+//    split K, each lane loads its MFMA operands straight from global memory
+//    with 16-byte loads (every weight byte is read once), and the partial
+//    sums meet in LDS.
+//
+// Within one 128-byte K slice, lane group g (lane / 16) of an MFMA operand
+// holds the 16-byte chunks g and g + 4 of its row. A and W use the same
+// assignment, so the product is the full dot product over the slice.
+#include "device.h"
+#include "launch.h"
+
+namespace w8a8 {
+namespace {
+
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Round-robin dispatch puts workgroup b on XCD b % 8. Renumber so that
+// each XCD gets a contiguous run of tile ids, then walk tile ids in groups
+// of G tile rows so that concurrently running tiles share A and W panels.
+template <int G>
+__device__ inline void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int per = total >> 3;
+  int t = bid;
+  if (bid < (per << 3)) t = (bid & 7) * per + (bid >> 3);
+  const int span = G * tiles_n;
+  const int group = t / span;
+  const int first_m = group * G;
+  const int gsize = min(tiles_m - first_m, G);
+  const int within = t - group * span;
+  tm = first_m + within % gsize;
+  tn = within / gsize;
+}
+
+template <int BM, int BN>
+struct Tiled {
+  static constexpr int kThreads = 256;
+  static constexpr int WM = BM / 2, WN = BN / 2;       // per-wave tile (2 x 2 waves)
+  static constexpr int SM = WM / 16, SN = WN / 16;     // 16x16 MFMA tiles per wave
+  static constexpr int kRows = BM + BN;                // rows of one K-slice stage
+  static constexpr int kStage = kRows * 128;           // bytes per stage
+  static constexpr int kLoads = kRows * 8 / kThreads;  // 16-byte loads per thread per stage
+  static constexpr int kEpiStride = BN * 2 + 16;       // bytes per staged output row
+  static constexpr int kEpi = BM * kEpiStride;
+  static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
+  static_assert((kRows * 8) % kThreads == 0, "stage must split evenly over the threads");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+};
+
+// Byte offset of logical 16-byte chunk c of a staged row. The XOR spreads
+// the 16 rows read by one MFMA operand load over distinct LDS banks.
+__device__ inline int stage_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                const uint8_t* __restrict__ W, const float* __restrict__ sw,
+                uint16_t* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
+  using C = Tiled<BM, BN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps rsrc / LDS bases scalar
+  int tm, tn;
+  map_tile<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  const auto rA = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
+
+  // Loader: slot s = tid + 256 i is a 16-byte LDS slot; rows 0..BN-1 of a
+  // stage hold W, rows BN.. hold A. Lanes of a wave fill consecutive slots,
+  // and pick the global chunk that belongs in their slot.
+  uint32_t goff[C::kLoads];
+  int gchunk[C::kLoads];
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    const int s = tid + C::kThreads * i;
+    const int row = s >> 3;
+    const int c = (s & 7) ^ ((row >> 1) & 7);
+    const int lrow = row < BN ? row : row - BN;
+    goff[i] = (uint32_t)lrow * (uint32_t)K + (uint32_t)(c << 4);
+    gchunk[i] = c << 4;
+  }
+  auto issue = [&](int stage, int k0) {
+    uint8_t* base = smem + stage * C::kStage;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int s0 = wave * 64 + C::kThreads * i;  // first slot of this wave's 64
+      const bool isW = (s0 >> 3) < BN;              // a wave's 8 rows lie on one side
+      const uint32_t off = (k0 + gchunk[i] < K) ? goff[i] + (uint32_t)k0 : kOutOfRange;
+      if (isW) buffer_load16_lds(rW, base + s0 * 16, off);
+      else     buffer_load16_lds(rA, base + s0 * 16, off);
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, g = lane >> 4;
+  v4f acc[C::SN][C::SM];
+#pragma unroll
+  for (int i = 0; i < C::SN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + 127) >> 7;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmem_all();
+    __syncthreads();
+    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
+    const uint8_t* st = smem + (kt & 1) * C::kStage;
+    v8i xf[C::SM];
+#pragma unroll
+    for (int j = 0; j < C::SM; ++j) {
+      const int row = BN + wm * C::WM + j * 16 + r16;
+      const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
+      const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
+      xf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+#pragma unroll
+    for (int i = 0; i < C::SN; ++i) {
+      const int row = wn * C::WN + i * 16 + r16;
+      const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
+      const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
+      const v8i wf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf, xf[j], acc[i][j]);
+    }
+  }
+
+  // Epilogue. acc[i][j][r] is Y[m][n] with m = m-tile j, lane % 16 and
+  // n = n-tile i, 4 * (lane / 16) + r: four consecutive outputs of one row.
+  __syncthreads();
+  float sA[C::SM];
+#pragma unroll
+  for (int j = 0; j < C::SM; ++j) {
+    const int m = m0 + wm * C::WM + j * 16 + r16;
+    sA[j] = m < M ? sa[m] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < C::SN; ++i) {
+    const int nl = wn * C::WN + i * 16 + 4 * g;
+    float4 sW = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (n0 + nl < N) sW = *reinterpret_cast<const float4*>(sw + n0 + nl);
+#pragma unroll
+    for (int j = 0; j < C::SM; ++j) {
+      const int ml = wm * C::WM + j * 16 + r16;
+      const v4f a = acc[i][j];
+      const uint32_t b0 = f32_to_bf16_rne(a[0] * sA[j] * sW.x);
+      const uint32_t b1 = f32_to_bf16_rne(a[1] * sA[j] * sW.y);
+      const uint32_t b2 = f32_to_bf16_rne(a[2] * sA[j] * sW.z);
+      const uint32_t b3 = f32_to_bf16_rne(a[3] * sA[j] * sW.w);
+      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = BN / 8;
+  for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
+    const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
+    const int m = m0 + row, n = n0 + col;
+    if (m < M && n < N)
+      *reinterpret_cast<uint4*>(Y + (int64_t)m * N + n) =
+          *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
+  }
+}
+
+// Small-M kernel: 16 weight rows per workgroup, K split over the 4 waves,
+// U K-steps of loads in flight per wave. MT = number of 16-token tiles.
+template <int MT, int U>
+__global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                                                   const uint8_t* __restrict__ W, const float* __restrict__ sw,
+                                                   uint16_t* __restrict__ Y, int M, int N, int K) {
+  __shared__ v4f red[3][MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 16;
+  const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  const auto rA = make_rsrc(A, (int64_t)M * K);
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t wrow = (uint32_t)r16 * (uint32_t)K;
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int nk = (K + 127) >> 7;
+  for (int kt = wave; kt < nk; kt += 4 * U) {
+    v8i wf[U], xf[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = (kt + 4 * u) << 7;
+      const int c0 = k0 + 16 * g, c1 = c0 + 64;
+      const bool live = kt + 4 * u < nk;
+      const uint32_t o0 = (live && c0 < K) ? (uint32_t)c0 : kOutOfRange;
+      const uint32_t o1 = (live && c1 < K) ? (uint32_t)c1 : kOutOfRange;
+      const v4i lo = buffer_load16(rW, o0 == kOutOfRange ? o0 : wrow + o0);
+      const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
+      wf[u] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const uint32_t xrow = (uint32_t)(t * 16 + r16) * (uint32_t)K;
+        const v4i xl = buffer_load16(rA, o0 == kOutOfRange ? o0 : xrow + o0);
+        const v4i xh = buffer_load16(rA, o1 == kOutOfRange ? o1 : xrow + o1);
+        xf[u][t] = v8i{xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+      }
+    }
+    // keep every load of this round ahead of the first MFMA: bytes in flight
+    // are what this kernel is limited by
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t] = mfma_16x16x128_e4m3(wf[u], xf[u][t], acc[t]);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int n = n0 + 4 * g;
+  if (n >= N) return;
+  const float4 sW = *reinterpret_cast<const float4*>(sw + n);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
+    const int m = t * 16 + r16;
+    if (m < M) {
+      const float s = sa[m];
+      const uint32_t b0 = f32_to_bf16_rne(a[0] * s * sW.x);
+      const uint32_t b1 = f32_to_bf16_rne(a[1] * s * sW.y);
+      const uint32_t b2 = f32_to_bf16_rne(a[2] * s * sW.z);
+      const uint32_t b3 = f32_to_bf16_rne(a[3] * s * sW.w);
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+  }
+}
+
+template <int BM, int BN>
+hipError_t run_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
+                     int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_tiled<BM, BN>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, a, sa, w, sw, y,
+                     (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M <= 16) {
+    hipLaunchKernelGGL((gemm_skinny<1, 4>), dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, a, sa, w, sw,
+                       y, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+  }
+  if (M <= 32) {
+    hipLaunchKernelGGL((gemm_skinny<2, 4>), dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, a, sa, w, sw,
+                       y, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+  }
+  return run_tiled<256, 192>(a, sa, w, sw, y, M, N, K, stream);
+}
+
+}  // namespace w8a8

@@ -1,0 +1,36 @@
+// Internal launchers behind the C ABI (include/w8a8.h). Arguments are
+// validated by the ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Per-row quantiser: x bf16 [M,K] -> q e4m3 [M,K], scale f32 [M].
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scale,
+                                hipStream_t stream);
+
+// Dense scaled FP8 GEMM: y[m,n] = bf16(sa[m] * sw[n] * sum_k a[m,k] w[n,k]).
+hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                       uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Routed-expert pipeline (moe.hip).
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, void* scratch, hipStream_t stream);
+
+hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids,
+                                  const uint8_t* w13, const float* s13, uint16_t* gu,
+                                  int32_t* perm, int64_t T, int64_t H, int64_t I, int64_t E,
+                                  int64_t topk, void* ws, hipStream_t stream);
+
+hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, const float* tw,
+                      const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
+                      uint16_t* out, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                      void* ws, hipStream_t stream);
+
+}  // namespace w8a8

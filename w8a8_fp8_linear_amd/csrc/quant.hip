@@ -1,0 +1,132 @@
+// Per-row dynamic FP8 quantisation (activations per token, weights per
+// output row).
+//
+// The pages quantise activations per token at run time and weights with one
+// scale per output channel (Lernex/Metis-1.6-Logos-FP8, "What is in FP8";
+// Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4": one scale per output
+// row). For a row x: amax = max|x| (exact, on the BF16 bit patterns),
+// s = fl32(amax / 448) (s = 1 for an all-zero row), q = E4M3(fl32(x / s))
+// with round to nearest even and saturation at 448.
+//
+// One wave per row: BF16 is read with 16-byte loads (8 values per lane per
+// load) and kept in registers, amax is a wave-wide max, then every element
+// is divided by s with a correctly rounded float32 division and encoded.
+// Rows longer than 64 * 8 * 16 values stream through twice instead.
+#include "device.h"
+#include "launch.h"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wave per row, 256 threads
+
+__device__ inline uint32_t absmax8(uint4 v) {
+  uint32_t m = 0;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+// 8 BF16 values -> 8 E4M3 codes (little-endian, element 0 in byte 0).
+__device__ inline uint2 quant8(uint4 v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = e4m3_rne_sat(bf16_lo(w[i]) / s);
+    c[2 * i + 1] = e4m3_rne_sat(bf16_hi(w[i]) / s);
+  }
+  uint2 r;
+  r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  return r;
+}
+
+__device__ inline float row_scale(uint32_t amax_bits) {
+  if (amax_bits == 0) return 1.0f;
+  return __uint_as_float(amax_bits << 16) / 448.0f;
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t M,
+                                                        int64_t K, uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nch = (int)(K >> 3);
+  const v4i* xr = reinterpret_cast<const v4i*>(x + row * K);
+  uint4 v[NCH];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    v4i t = v4i{0, 0, 0, 0};
+    if (c < nch) t = __builtin_nontemporal_load(xr + c);
+    v[i] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const uint32_t m = absmax8(v[i]);
+    amax = amax > m ? amax : m;
+  }
+  amax = wave_max_u32(amax);
+  const float s = row_scale(amax);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) qr[c] = quant8(v[i], s);
+  }
+  if (lane == 0) scale[row] = s;
+}
+
+__global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restrict__ x, int64_t M,
+                                                          int64_t K, uint8_t* __restrict__ q,
+                                                          float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int64_t nch = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  uint32_t amax = 0;
+  for (int64_t c = lane; c < nch; c += 64) {
+    const uint32_t m = absmax8(xr[c]);
+    amax = amax > m ? amax : m;
+  }
+  amax = wave_max_u32(amax);
+  const float s = row_scale(amax);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+  for (int64_t c = lane; c < nch; c += 64) qr[c] = quant8(xr[c], s);
+  if (lane == 0) scale[row] = s;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scale,
+                                hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 block(64 * kRowsPerBlock);
+  const int64_t per_lane = (K / 8 + 63) / 64;  // 16-byte chunks per lane
+  if (per_lane <= 1)
+    hipLaunchKernelGGL(quant_rows_regs<1>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL(quant_rows_regs<2>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL(quant_rows_regs<4>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL(quant_rows_regs<8>, grid, block, 0, stream, x, M, K, q, scale);
+  else if (per_lane <= 16)
+    hipLaunchKernelGGL(quant_rows_regs<16>, grid, block, 0, stream, x, M, K, q, scale);
+  else
+    hipLaunchKernelGGL(quant_rows_stream, grid, block, 0, stream, x, M, K, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8
