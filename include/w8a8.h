@@ -113,6 +113,117 @@ int quantize_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, uint8_t* q_
 int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
               uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+
+/* ---------------------------------------------------------------------------
+ * Routed experts
+ *
+ * The routed experts are FP8 with the same scheme (Lernex/Metis-1.6-Logos-FP8,
+ * "What is in FP8"); each token goes to its top-k experts (Lernex/Metis-1.6-
+ * Praxis, "Architecture"); experts are stacked in global expert order (the
+ * "Files" section of the model pages); the stack, and so this expert stage,
+ * runs twice per token with one set of weights (sglang-metis 0.1.0, "How the
+ * model maps onto SGLang"). Readings taken where the pages are silent: W13[e]
+ * holds [gate; up] rows, the activation is h = silu(g) * u in float32, h is
+ * requantised with one E4M3 scale per routed copy, the k outputs of a token
+ * are weighted by its router weights, summed in float32 and rounded once to
+ * BF16.
+ *
+ * Shapes (all row-major)
+ *   x_q      [T, H]       E4M3 tokens, quantised once per token (quantize_per_token)
+ *   x_scale  [T]          float32
+ *   topk_ids [T, topk]    int32 expert ids; ids outside [0, E) are dropped
+ *   topk_w   [T, topk]    float32 router weights (used as given)
+ *   w13_q    [E, 2I, H]   E4M3; rows 0..I-1 gate, rows I..2I-1 up
+ *   w13_scale[E, 2I]      float32 per output row
+ *   w2_q     [E, H, I]    E4M3
+ *   w2_scale [E, H]       float32 per output row
+ * A slot is the flat index t * topk + j. The expert-sorted order lists the
+ * valid slots grouped by expert id, increasing slot index inside an expert.
+ * Limits: 1 <= E <= 1024, 1 <= topk <= 64, H and I positive multiples of 16,
+ * T * topk, T * H and 2 * I * H below 2^31. The fused calls need I = 256 or
+ * 512. T == 0 is a no-op. offsets/perm passed to the stage calls must come
+ * from moe_route (they are read on the device, never on the host).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of scratch moe_route needs (0 for invalid sizes). */
+size_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+
+/*
+ * moe_route — expert-sorted permutation of the routed slots.
+ *   counts  [E]       number of valid slots per expert
+ *   offsets [E + 1]   exclusive prefix of counts; offsets[E] = valid slots
+ *   perm    [T*topk]  perm[offsets[e] + i] = i-th slot (increasing) routed
+ *                     to e; entries from offsets[E] on are set to -1
+ *   workspace         device scratch of moe_route_workspace_bytes bytes
+ * Bit-exact, deterministic. Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED,
+ * MISALIGNED, WORKSPACE, DEVICE, LAUNCH.
+ */
+int moe_route(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* counts, int32_t* offsets,
+              int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_gate_up_bf16 — grouped gate/up projection, BF16 result.
+ *   gu_bf16[r, :] = bf16( x_scale[t] * w13_scale[e, :] * (x_q[t, :] . w13_q[e]^T) )
+ * for the r-th sorted slot (t = perm[r] / topk, e its expert); gu_bf16 is
+ * [T*topk, 2I], rows from offsets[E] on are left untouched.
+ */
+int moe_gate_up_bf16(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
+                     const uint8_t* w13_q, const float* w13_scale, uint16_t* gu_bf16, int64_t T, int64_t H,
+                     int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+
+/*
+ * moe_gate_up_swiglu_quant — grouped gate/up projection with the expert
+ * activation and the requantisation fused in:
+ *   g, u = the gate and up halves of the slot's float32 gate/up row
+ *   h    = silu(g) * u                       (float32)
+ *   h_scale[r] = fl32(max|h| / 448) (1 if h == 0),
+ *   h_q[r, i]  = E4M3(fl32(h[i] / h_scale[r]))  (round to nearest even, saturating)
+ *   h_q [T*topk, I], h_scale [T*topk], both in sorted order. I = 256 or 512.
+ */
+int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
+                             const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q, float* h_scale, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+
+/*
+ * moe_down_combine — grouped down projection and router-weighted combine:
+ *   y[r, :]      = h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T)
+ *   out_bf16[t]  = bf16( sum over the token's valid slots of topk_w[slot] * y )
+ * Sums are float32 (atomic, so their order, and the last bit of a sum, can
+ * vary between runs). acc_f32 [T, H] is caller-provided scratch; it is
+ * cleared by the call. A token with no valid slot gets zeros.
+ */
+int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
+                     const float* topk_w, const uint8_t* w2_q, const float* w2_scale, uint16_t* out_bf16,
+                     float* acc_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+
+/* Bytes of scratch w8a8_grouped_gemm needs (0 for invalid sizes). */
+size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+
+/*
+ * w8a8_grouped_gemm — moe_route followed by moe_gate_up_bf16: the routed
+ * gate/up grouped GEMM on per-token FP8 activations with a BF16 result.
+ * Outputs gu_bf16 [T*topk, 2I] in sorted order, perm [T*topk] and
+ * offsets [E + 1] (as moe_route) so the caller can map rows back to slots.
+ */
+int w8a8_grouped_gemm(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const uint8_t* w13_q,
+                      const float* w13_scale, uint16_t* gu_bf16, int32_t* perm, int32_t* offsets, int64_t T,
+                      int64_t H, int64_t I, int64_t E, int64_t topk, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Bytes of scratch moe_w8a8_grouped needs (0 for invalid sizes). */
+size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+
+/*
+ * moe_w8a8_grouped — one routed-expert pass: moe_route, then
+ * moe_gate_up_swiglu_quant, then moe_down_combine, on buffers carved from
+ * `workspace`. out_bf16 [T, H]. Running the stack's two passes is two calls,
+ * the second on quantize_per_token of the first call's output.
+ */
+int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const float* topk_w,
+                     const uint8_t* w13_q, const float* w13_scale, const uint8_t* w2_q, const float* w2_scale,
+                     uint16_t* out_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,17 @@ U32 = 2.0 ** -24  # float32 unit roundoff
 MFMA_GROUP_ERR = 2.0 ** -10  # E4M3 MFMA: 8 products x 2**-13 of the group maximum
 
 
+def record(name: str, rep: dict) -> None:
+    """Append a parity report to $W8A8_PARITY_LOG (JSON lines), if set."""
+    import json
+    import os
+
+    path = os.environ.get("W8A8_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": name, **rep}) + "\n")
+
+
 def to_dev_bf16(bits: np.ndarray):
     import torch
 

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import bf16_bits, gemm_report, to_dev, to_dev_bf16
+from gpu_util import bf16_bits, gemm_report, record, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -145,6 +145,7 @@ def test_gemm_parity(name, M, N, K):
     got = _run_gemm(qx, sx, qw, sw)
     rep = gemm_report(got, qx, sx, qw, sw)
     print(name, rep, flush=True)
+    record(f"gemm {name}", rep)
     assert rep["n_bound_violations"] == 0, rep
     assert rep["frobenius"] <= 4e-3, rep
 
@@ -164,6 +165,7 @@ def test_gemm_prefill_full_size():
     qw, sw, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["w"]))
     rep = gemm_report(got, qx, sx, qw, sw)
     print("prefill", rep, flush=True)
+    record("gemm prefill 4096x2048->6144 (full)", rep)
     assert rep["n_bound_violations"] == 0, rep
     assert rep["frobenius"] <= 4e-3, rep
     # The literal max-abs criterion (1e-2 * rms) is reported, not asserted:

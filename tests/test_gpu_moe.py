@@ -1,0 +1,237 @@
+"""GPU parity of the routed-expert path against the oracle.
+
+* moe_route: counts, offsets and the permutation are bit-exact.
+* Gate/up (BF16 result): every element inside the E4M3 matrix-core bound.
+* Fused SwiGLU + requantisation: scales within the propagated bound and
+  every code explainable (differs from the oracle's only where the oracle's
+  scaled value lies within the propagated error of a rounding boundary).
+* Down + combine: fed the GPU's own requantised rows, every output element
+  of the sampled tokens inside the bound.
+* Full pass and the two-pass stack: normalised Frobenius <= 4e-3 against the
+  oracle, pass 2 teacher-forced with the GPU's pass-1 output.
+Shapes: the routed-expert workloads (4096 and 16384 tokens, H 2048, I 512,
+64 experts, top-8, Zipf routing) and small ragged ones.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import bf16_bits, record, to_dev
+from moe_util import (bf16_compare, check_requant, down_combine_ref, quantized_moe,
+                      sorted_rows_gate_up)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import w8a8_fp8_linear_amd as w8  # noqa: E402
+
+SMALL = dict(T=37, H=256, I=256, E=5, k=3, n_outlier=2)
+GATE_UP = dict(T=4096, H=2048, I=512, E=64, k=8, n_outlier=20)
+TWO_PASS = dict(T=16384, H=2048, I=512, E=64, k=8, n_outlier=20, passes=2)
+
+
+@pytest.fixture(scope="module")
+def small():
+    d = quantized_moe(**SMALL, seed=5)
+    ids, w = d["routes"][0]
+    ids = ids.copy()
+    ids[3, 1] = -1          # dropped slots
+    ids[10, 0] = SMALL["E"]
+    d["routes"][0] = (ids, w)
+    return d
+
+
+@pytest.fixture(scope="module")
+def gate_up_cfg():
+    return quantized_moe(**GATE_UP, seed=0)
+
+
+@pytest.fixture(scope="module")
+def two_pass_cfg():
+    return quantized_moe(**TWO_PASS, seed=0)
+
+
+def _dev(d):
+    return {"qx": to_dev(d["qx"]), "sx": to_dev(d["sx"]), "q13": to_dev(d["q13"]), "s13": to_dev(d["s13"]),
+            "q2": to_dev(d["q2"]), "s2": to_dev(d["s2"])}
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (37, 3, 5), (1000, 8, 7), (4096, 8, 64), (16384, 8, 64),
+                                   (513, 4, 130), (2000, 2, 1024)])
+def test_route_bitexact(T, k, E):
+    print(f"[route] T={T} k={k} E={E}", flush=True)
+    rng = np.random.default_rng(T + k + E)
+    ids = rng.integers(-1, E + 1, (T, k)).astype(np.int32)
+    if E == 64:
+        from synth import routing
+        ids, _ = routing(rng, T, E, k)
+    counts, offsets, perm = w8.moe_route(to_dev(ids), E)
+    torch.cuda.synchronize()
+    rc, ro, rp = oracle.route(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    p = perm.cpu().numpy()
+    assert np.array_equal(p[:rp.size], rp)
+    assert np.all(p[rp.size:] == -1)
+
+
+def test_route_deterministic():
+    from synth import routing
+    ids, _ = routing(np.random.default_rng(1), 4096, 64, 8)
+    a = w8.moe_route(to_dev(ids), 64)[2].cpu().numpy()
+    b = w8.moe_route(to_dev(ids), 64)[2].cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def _check_gate_up_bf16(d, sample=None):
+    dv = _dev(d)
+    ids, _ = d["routes"][0]
+    gu, perm, offsets = w8.w8a8_grouped_gemm(dv["qx"], dv["sx"], to_dev(ids), dv["q13"], dv["s13"])
+    torch.cuda.synchronize()
+    _, ro, rp = oracle.route(ids, d["E"])
+    assert np.array_equal(perm.cpu().numpy()[:rp.size], rp)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    rows = np.arange(rp.size) if sample is None else np.sort(
+        np.random.default_rng(0).choice(rp.size, min(sample, rp.size), replace=False))
+    gu64, err = sorted_rows_gate_up(d["qx"], d["sx"], ids, rp, rows, d["q13"], d["s13"], d["k"])
+    got = bf16_bits(gu)[rows]
+    rep = bf16_compare(got, gu64, err)
+    print("gate/up bf16", rep, flush=True)
+    record(f"moe gate/up bf16 T={d['T']} E={d['E']} k={d['k']}", rep)
+    assert rep["n_bound_violations"] == 0, rep
+    assert rep["frobenius"] <= 4e-3, rep
+
+
+def test_gate_up_bf16_small(small):
+    _check_gate_up_bf16(small)
+
+
+def test_gate_up_bf16_full_size(gate_up_cfg):
+    """4096 tokens, top-8 of 64 experts, [1024 x 2048] gate+up per expert: every row."""
+    _check_gate_up_bf16(gate_up_cfg)
+
+
+def _check_fused_requant(d, route_idx=0, sample=None):
+    dv = _dev(d)
+    ids, _ = d["routes"][route_idx]
+    counts, offsets, perm = w8.moe_route(to_dev(ids), d["E"])
+    hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, offsets, dv["q13"], dv["s13"], d["k"])
+    torch.cuda.synchronize()
+    _, _, rp = oracle.route(ids, d["E"])
+    rows = np.arange(rp.size) if sample is None else np.sort(
+        np.random.default_rng(1).choice(rp.size, min(sample, rp.size), replace=False))
+    gu64, err = sorted_rows_gate_up(d["qx"], d["sx"], ids, rp, rows, d["q13"], d["s13"], d["k"])
+    rep = check_requant(hq.cpu().numpy()[rows], hs.cpu().numpy()[rows], gu64, err)
+    print("fused requant", rep, flush=True)
+    record(f"moe fused swiglu+requant T={d['T']} E={d['E']} k={d['k']} rows={len(rows)}", rep)
+    return hq, hs, perm, offsets
+
+
+def test_fused_requant_small(small):
+    _check_fused_requant(small)
+
+
+def test_fused_requant_gate_up_cfg(gate_up_cfg):
+    _check_fused_requant(gate_up_cfg, sample=4096)
+
+
+def _check_down(d, hq, hs, perm, offsets, route_idx=0, n_tokens=None):
+    dv = _dev(d)
+    ids, tw = d["routes"][route_idx]
+    out = w8.moe_down_combine(hq, hs, perm, offsets, to_dev(tw), dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    T = d["T"]
+    tokens = np.arange(T) if n_tokens is None else np.sort(
+        np.random.default_rng(2).choice(T, n_tokens, replace=False))
+    ref64, err = down_combine_ref(hq.cpu().numpy(), hs.cpu().numpy(), perm.cpu().numpy(), ids, tw,
+                                  d["q2"], d["s2"], d["k"], tokens)
+    rep = bf16_compare(bf16_bits(out)[tokens], ref64, err)
+    print("down+combine", rep, flush=True)
+    record(f"moe down+combine T={d['T']} tokens={len(tokens)}", rep)
+    assert rep["n_bound_violations"] == 0, rep
+    assert rep["frobenius"] <= 4e-3, rep
+
+
+def test_down_combine_small(small):
+    hq, hs, perm, offsets = _check_fused_requant(small)
+    _check_down(small, hq, hs, perm, offsets)
+
+
+def test_down_combine_two_pass_cfg(two_pass_cfg):
+    hq, hs, perm, offsets = _check_fused_requant(two_pass_cfg, sample=4096)
+    _check_down(two_pass_cfg, hq, hs, perm, offsets, n_tokens=512)
+
+
+def _oracle_pass_tokens(qx, sx, ids, w, d, tokens):
+    out64, _, _ = oracle.moe_pass(qx[tokens], sx[tokens], ids[tokens], w[tokens], d["q13"], d["s13"],
+                                  d["q2"], d["s2"])
+    return out64
+
+
+def test_full_pass_small(small):
+    dv = _dev(small)
+    ids, w = small["routes"][0]
+    out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    ref64 = _oracle_pass_tokens(small["qx"], small["sx"], ids, w, small, np.arange(small["T"]))
+    rep = bf16_compare(bf16_bits(out), ref64)
+    print("full pass small", rep, flush=True)
+    record("moe full pass small", rep)
+    assert rep["frobenius"] <= 4e-3, rep
+
+
+def test_two_pass_stack(two_pass_cfg):
+    """16384 tokens, two passes with the same weights; 384 sampled tokens per pass.
+    Pass 2 is teacher-forced: the oracle's pass 2 starts from the GPU's pass-1 output."""
+    d = two_pass_cfg
+    dv = _dev(d)
+    routes_dev = [(to_dev(i), to_dev(w)) for i, w in d["routes"]]
+    from gpu_util import to_dev_bf16
+    x = to_dev_bf16(d["x_bits"])
+    ws = w8.moe_workspace(d["T"], d["H"], d["I"], d["E"], d["k"])
+    outs = w8.moe_ffn(x, routes_dev, dv["q13"], dv["s13"], dv["q2"], dv["s2"], workspace=ws)
+    torch.cuda.synchronize()
+    tokens = np.sort(np.random.default_rng(3).choice(d["T"], 384, replace=False))
+    # pass 1 from the oracle's own quantised input
+    ids1, w1 = d["routes"][0]
+    ref1 = _oracle_pass_tokens(d["qx"], d["sx"], ids1, w1, d, tokens)
+    p1_bits = bf16_bits(outs[0])
+    rep1 = bf16_compare(p1_bits[tokens], ref1)
+    print("pass 1", rep1, flush=True)
+    record("moe two-pass T=16384 pass 1 (384 tokens)", rep1)
+    assert rep1["frobenius"] <= 4e-3, rep1
+    # pass 2 from the GPU's pass-1 output (teacher forcing)
+    x2 = oracle.bf16_bits_to_f64(p1_bits[tokens]).astype(np.float32)
+    qx2, sx2, _ = oracle.quantize_rows(x2)
+    ids2, w2 = d["routes"][1]
+    ref2, _, _ = oracle.moe_pass(qx2, sx2, ids2[tokens], w2[tokens], d["q13"], d["s13"], d["q2"], d["s2"])
+    rep2 = bf16_compare(bf16_bits(outs[1])[tokens], ref2)
+    print("pass 2 (teacher-forced)", rep2, flush=True)
+    record("moe two-pass T=16384 pass 2 teacher-forced (384 tokens)", rep2)
+    assert rep2["frobenius"] <= 4e-3, rep2
+
+
+def test_all_slots_dropped_gives_zeros(small):
+    dv = _dev(small)
+    T, k = small["T"], small["k"]
+    ids = np.full((T, k), -1, np.int32)
+    w = np.ones((T, k), np.float32)
+    out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    assert not bf16_bits(out).any()
+
+
+def test_moe_argument_errors(small):
+    dv = _dev(small)
+    ids = torch.zeros((small["T"], small["k"]), dtype=torch.int32, device="cuda")
+    w = torch.ones((small["T"], small["k"]), dtype=torch.float32, device="cuda")
+    q13 = torch.zeros((small["E"], 2 * 48, small["H"]), dtype=torch.uint8, device="cuda")
+    s13 = torch.ones((small["E"], 2 * 48), dtype=torch.float32, device="cuda")
+    q2 = torch.zeros((small["E"], small["H"], 48), dtype=torch.uint8, device="cuda")
+    s2 = torch.ones((small["E"], small["H"]), dtype=torch.float32, device="cuda")
+    with pytest.raises(w8.W8A8Error) as e:
+        w8.moe_w8a8_grouped(dv["qx"], dv["sx"], ids, w, q13, s13, q2, s2)   # I = 48 has no fused kernel
+    assert e.value.status == 4

@@ -18,6 +18,8 @@ import os
 __all__ = [
     "W8A8Error", "lib", "lib_path", "abi_version",
     "quantize_per_token", "w8a8_gemm", "w8a8_linear", "quantize_weight",
+    "moe_route", "moe_gate_up_bf16", "moe_gate_up_swiglu_quant", "moe_down_combine",
+    "w8a8_grouped_gemm", "moe_w8a8_grouped", "moe_workspace", "moe_ffn",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +35,16 @@ _SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quantize_per_token": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "w8a8_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
+    "moe_route_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "moe_route": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
+                                 _c_ptr]),
+    "moe_gate_up_bf16": (ctypes.c_int, [_c_ptr] * 7 + [_c_i64] * 5 + [_c_ptr]),
+    "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr]),
+    "moe_down_combine": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [_c_ptr]),
+    "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "w8a8_grouped_gemm": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
+    "moe_w8a8_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 5),
+    "moe_w8a8_grouped": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
 }
 
 
@@ -157,3 +169,150 @@ def w8a8_linear(x, w_q, w_scale, out=None):
     """The layer: quantise the BF16 input per token, then the scaled FP8 GEMM."""
     q, s = quantize_per_token(x)
     return w8a8_gemm(q, s, w_q, w_scale, out=out)
+
+
+# ---- routed experts -----------------------------------------------------------
+#
+# Shapes: x_q [T, H] uint8 (E4M3), x_scale [T] f32, topk_ids [T, k] int32,
+# topk_w [T, k] f32, w13_q [E, 2I, H] uint8 ([gate; up] rows), w13_scale
+# [E, 2I] f32, w2_q [E, H, I] uint8, w2_scale [E, H] f32. Slots are t*k + j;
+# "sorted" arrays list the valid slots grouped by expert (stable).
+
+
+def _moe_dims(x_q, topk_ids, w13_q):
+    T, H = x_q.shape
+    E, twoI, H2 = w13_q.shape
+    if H2 != H or twoI % 2:
+        raise ValueError("w13_q must be [E, 2I, H]")
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must be [T, k]")
+    return T, H, twoI // 2, E, topk_ids.shape[1]
+
+
+def moe_route(topk_ids, E: int):
+    """Expert-sorted order of the routed slots: (counts [E], offsets [E+1], perm [T*k]) int32."""
+    import torch
+
+    _want(topk_ids, torch.int32, 2, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nbytes = max(int(lib().moe_route_workspace_bytes(T, k, E)), 16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check("moe_route", lib().moe_route(topk_ids.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
+                                        perm.data_ptr(), ws.data_ptr(), nbytes, _stream(topk_ids)))
+    return counts, offsets, perm
+
+
+def moe_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int):
+    """Sorted-slot gate/up rows in BF16: [T*k, 2I]."""
+    import torch
+
+    T, H = x_q.shape
+    E, twoI, _ = w13_q.shape
+    gu = torch.empty((T * topk, twoI), dtype=torch.bfloat16, device=x_q.device)
+    _check("moe_gate_up_bf16", lib().moe_gate_up_bf16(
+        x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), w13_q.data_ptr(),
+        w13_scale.data_ptr(), gu.data_ptr(), T, H, twoI // 2, E, topk, _stream(x_q)))
+    return gu
+
+
+def moe_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int):
+    """Sorted-slot requantised h = silu(g) * u: (h_q uint8 [T*k, I], h_scale f32 [T*k])."""
+    import torch
+
+    T, H = x_q.shape
+    E, twoI, _ = w13_q.shape
+    I = twoI // 2
+    h_q = torch.empty((T * topk, I), dtype=torch.uint8, device=x_q.device)
+    h_s = torch.empty((T * topk,), dtype=torch.float32, device=x_q.device)
+    _check("moe_gate_up_swiglu_quant", lib().moe_gate_up_swiglu_quant(
+        x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), w13_q.data_ptr(),
+        w13_scale.data_ptr(), h_q.data_ptr(), h_s.data_ptr(), T, H, I, E, topk, _stream(x_q)))
+    return h_q, h_s
+
+
+def moe_down_combine(h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out=None, acc=None):
+    """Down projection of the sorted slots and the router-weighted combine: BF16 [T, H]."""
+    import torch
+
+    T, k = topk_w.shape
+    E, H, I = w2_q.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
+    if acc is None:
+        acc = torch.empty((T, H), dtype=torch.float32, device=h_q.device)
+    _check("moe_down_combine", lib().moe_down_combine(
+        h_q.data_ptr(), h_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), topk_w.data_ptr(),
+        w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), acc.data_ptr(), T, H, I, E, k, _stream(h_q)))
+    return out
+
+
+def w8a8_grouped_gemm(x_q, x_scale, topk_ids, w13_q, w13_scale):
+    """Routing + BF16 gate/up grouped GEMM: (gu [T*k, 2I] sorted, perm [T*k], offsets [E+1])."""
+    import torch
+
+    for t, dt, nd, n in ((x_q, torch.uint8, 2, "x_q"), (x_scale, torch.float32, 1, "x_scale"),
+                         (topk_ids, torch.int32, 2, "topk_ids"), (w13_q, torch.uint8, 3, "w13_q"),
+                         (w13_scale, torch.float32, 2, "w13_scale")):
+        _want(t, dt, nd, n)
+    T, H, I, E, k = _moe_dims(x_q, topk_ids, w13_q)
+    dev = x_q.device
+    gu = torch.empty((T * k, 2 * I), dtype=torch.bfloat16, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    nbytes = max(int(lib().w8a8_grouped_gemm_workspace_bytes(T, k, E)), 16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check("w8a8_grouped_gemm", lib().w8a8_grouped_gemm(
+        x_q.data_ptr(), x_scale.data_ptr(), topk_ids.data_ptr(), w13_q.data_ptr(), w13_scale.data_ptr(),
+        gu.data_ptr(), perm.data_ptr(), offsets.data_ptr(), T, H, I, E, k, ws.data_ptr(), nbytes, _stream(x_q)))
+    return gu, perm, offsets
+
+
+def moe_workspace(T: int, H: int, I: int, E: int, topk: int, device="cuda"):
+    """Scratch buffer sized for moe_w8a8_grouped."""
+    import torch
+
+    nbytes = int(lib().moe_w8a8_workspace_bytes(T, H, I, E, topk))
+    if nbytes == 0 and T > 0:
+        raise ValueError("unsupported routed-expert sizes")
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def moe_w8a8_grouped(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out=None, workspace=None):
+    """One routed-expert pass on per-token FP8 tokens: BF16 [T, H]."""
+    import torch
+
+    for t, dt, nd, n in ((x_q, torch.uint8, 2, "x_q"), (x_scale, torch.float32, 1, "x_scale"),
+                         (topk_ids, torch.int32, 2, "topk_ids"), (topk_w, torch.float32, 2, "topk_w"),
+                         (w13_q, torch.uint8, 3, "w13_q"), (w13_scale, torch.float32, 2, "w13_scale"),
+                         (w2_q, torch.uint8, 3, "w2_q"), (w2_scale, torch.float32, 2, "w2_scale")):
+        _want(t, dt, nd, n)
+    T, H, I, E, k = _moe_dims(x_q, topk_ids, w13_q)
+    if tuple(w2_q.shape) != (E, H, I) or tuple(topk_w.shape) != (T, k):
+        raise ValueError("w2_q must be [E, H, I] and topk_w [T, k]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x_q.device)
+    if workspace is None:
+        workspace = moe_workspace(T, H, I, E, k, device=x_q.device)
+    _check("moe_w8a8_grouped", lib().moe_w8a8_grouped(
+        x_q.data_ptr(), x_scale.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w13_q.data_ptr(),
+        w13_scale.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), T, H, I, E, k,
+        workspace.data_ptr(), workspace.numel(), _stream(x_q)))
+    return out
+
+
+def moe_ffn(x, routes, w13_q, w13_scale, w2_q, w2_scale, workspace=None):
+    """The routed-expert stage run once per entry of ``routes`` with the same
+    weights, each pass fed the previous pass's BF16 output (the stack runs
+    twice per token with shared weights; sglang-metis 0.1.0, "How the model
+    maps onto SGLang"). ``routes`` is a list of (topk_ids, topk_w). Returns the
+    list of per-pass BF16 outputs."""
+    outs = []
+    for ids, w in routes:
+        xq, xs = quantize_per_token(x)
+        x = moe_w8a8_grouped(xq, xs, ids, w, w13_q, w13_scale, w2_q, w2_scale, workspace=workspace)
+        outs.append(x)
+    return outs

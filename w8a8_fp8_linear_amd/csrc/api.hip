@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "../../include/w8a8.h"
 #include "launch.h"
@@ -90,6 +91,151 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_gemm(a_q, a_scale, w_q, w_scale, y_bf16, M, N, K, stream));
+}
+
+}  // extern "C"
+
+// ---- routed experts ---------------------------------------------------------
+namespace {
+
+constexpr int64_t kMaxExperts = 1024;
+constexpr int64_t kMaxTopk = 64;
+
+// Shared checks of the routed-expert calls. Returns W8A8_OK or a status.
+int check_moe_shape(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+  if (T < 0 || H < 0 || I < 0 || E < 0 || topk < 0) return W8A8_ERR_BAD_SHAPE;
+  if (!mul_ok(T, topk) || !mul_ok(T, H) || !mul_ok(T * H, 4)) return W8A8_ERR_BAD_SHAPE;
+  if (E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk) return W8A8_ERR_UNSUPPORTED;
+  if (H == 0 || H % 16 != 0 || I == 0 || I % 16 != 0) return W8A8_ERR_UNSUPPORTED;
+  // 32-bit element offsets inside the kernels
+  if (T * topk > INT32_MAX || T * H > INT32_MAX || 2 * I * H > INT32_MAX || T * topk * I > INT64_C(1) << 40)
+    return W8A8_ERR_UNSUPPORTED;
+  if (!mul_ok(E * 2 * I, H)) return W8A8_ERR_BAD_SHAPE;
+  return W8A8_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
+bool any_null(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return true;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
+  if (T < 0 || topk < 1 || E < 1 || !mul_ok(T, topk)) return 0;
+  return w8a8::route_workspace_bytes(T, topk, E);
+}
+
+int moe_route(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* counts, int32_t* offsets,
+              int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || topk < 0 || E < 0 || !mul_ok(T, topk)) return W8A8_ERR_BAD_SHAPE;
+  if (E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk || T * topk > INT32_MAX) return W8A8_ERR_UNSUPPORTED;
+  if (T == 0) return W8A8_OK;
+  if (any_null({topk_ids, counts, offsets, perm, workspace})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({topk_ids, counts, offsets, perm, workspace})) return W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < w8a8::route_workspace_bytes(T, topk, E)) return W8A8_ERR_WORKSPACE;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_route(topk_ids, T, topk, E, counts, offsets, perm, workspace, stream));
+}
+
+int moe_gate_up_bf16(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
+                     const uint8_t* w13_q, const float* w13_scale, uint16_t* gu_bf16, int64_t T, int64_t H, int64_t I,
+                     int64_t E, int64_t topk, hipStream_t stream) {
+  const int c = check_moe_shape(T, H, I, E, topk);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16})) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(
+      w8a8::launch_grouped_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16, T, H, I, E, topk, stream));
+}
+
+int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
+                             const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q, float* h_scale, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
+  const int c = check_moe_shape(T, H, I, E, topk);
+  if (c != W8A8_OK) return c;
+  if (I != 256 && I != 512) return W8A8_ERR_UNSUPPORTED;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale})) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale,
+                                                         T, H, I, E, topk, stream));
+}
+
+int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
+                     const float* topk_w, const uint8_t* w2_q, const float* w2_scale, uint16_t* out_bf16,
+                     float* acc_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
+  const int c = check_moe_shape(T, H, I, E, topk);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16, acc_f32})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16, acc_f32}))
+    return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16,
+                                                 acc_f32, T, H, I, E, topk, stream));
+}
+
+size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
+  if (T < 0 || topk < 1 || E < 1 || !mul_ok(T, topk)) return 0;
+  return w8a8::grouped_gate_up_workspace_bytes(T, topk, E);
+}
+
+int w8a8_grouped_gemm(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const uint8_t* w13_q,
+                      const float* w13_scale, uint16_t* gu_bf16, int32_t* perm, int32_t* offsets, int64_t T,
+                      int64_t H, int64_t I, int64_t E, int64_t topk, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  const int c = check_moe_shape(T, H, I, E, topk);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, topk_ids, w13_q, w13_scale, gu_bf16, perm, offsets, workspace})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, topk_ids, w13_q, w13_scale, gu_bf16, perm, offsets, workspace}))
+    return W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < w8a8::grouped_gate_up_workspace_bytes(T, topk, E)) return W8A8_ERR_WORKSPACE;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_grouped_gate_up(x_q, x_scale, topk_ids, w13_q, w13_scale, gu_bf16, perm, offsets,
+                                                    T, H, I, E, topk, workspace, stream));
+}
+
+size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+  if (check_moe_shape(T, H, I, E, topk) != W8A8_OK) return 0;
+  return w8a8::moe_workspace_bytes(T, H, I, E, topk);
+}
+
+int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const float* topk_w,
+                     const uint8_t* w13_q, const float* w13_scale, const uint8_t* w2_q, const float* w2_scale,
+                     uint16_t* out_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const int c = check_moe_shape(T, H, I, E, topk);
+  if (c != W8A8_OK) return c;
+  if (I != 256 && I != 512) return W8A8_ERR_UNSUPPORTED;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
+    return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
+    return W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < w8a8::moe_workspace_bytes(T, H, I, E, topk)) return W8A8_ERR_WORKSPACE;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_moe(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, T,
+                                        H, I, E, topk, workspace, stream));
 }
 
 }  // extern "C"

@@ -93,4 +93,33 @@ __device__ inline float wave_max_f32(float v) {
   return v;
 }
 
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Round-robin dispatch puts workgroup b on XCD b % 8. Renumber so that
+// each XCD gets a contiguous run of tile ids, then walk tile ids in groups
+// of G tile rows so that concurrently running tiles share A and W panels.
+template <int G>
+__device__ inline void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int per = total >> 3;
+  int t = bid;
+  if (bid < (per << 3)) t = (bid & 7) * per + (bid >> 3);
+  const int span = G * tiles_n;
+  const int group = t / span;
+  const int first_m = group * G;
+  const int gsize = min(tiles_m - first_m, G);
+  const int within = t - group * span;
+  tm = first_m + within % gsize;
+  tn = within / gsize;
+}
+
+// Byte offset of logical 16-byte chunk c of a staged row. The XOR spreads
+// the 16 rows read by one MFMA operand load over distinct LDS banks.
+__device__ inline int stage_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+
+// FP8 x FP8 -> FP32, 32x32 outputs, 64-deep (E4M3 both operands).
+__device__ inline v16f mfma_32x32x64_e4m3(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 }  // namespace w8a8

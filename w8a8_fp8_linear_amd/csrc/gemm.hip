@@ -31,26 +31,6 @@
 namespace w8a8 {
 namespace {
 
-__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-// Round-robin dispatch puts workgroup b on XCD b % 8. Renumber so that
-// each XCD gets a contiguous run of tile ids, then walk tile ids in groups
-// of G tile rows so that concurrently running tiles share A and W panels.
-template <int G>
-__device__ inline void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  const int per = total >> 3;
-  int t = bid;
-  if (bid < (per << 3)) t = (bid & 7) * per + (bid >> 3);
-  const int span = G * tiles_n;
-  const int group = t / span;
-  const int first_m = group * G;
-  const int gsize = min(tiles_m - first_m, G);
-  const int within = t - group * span;
-  tm = first_m + within % gsize;
-  tn = within / gsize;
-}
-
 template <int BM, int BN>
 struct Tiled {
   static constexpr int kThreads = 256;
@@ -65,10 +45,6 @@ struct Tiled {
   static_assert((kRows * 8) % kThreads == 0, "stage must split evenly over the threads");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
 };
-
-// Byte offset of logical 16-byte chunk c of a staged row. The XOR spreads
-// the 16 rows read by one MFMA operand load over distinct LDS banks.
-__device__ inline int stage_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 template <int BM, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -86,28 +62,23 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
   const auto rA = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
 
   // Loader: slot s = tid + 256 i is a 16-byte LDS slot; rows 0..BN-1 of a
-  // stage hold W, rows BN.. hold A. Lanes of a wave fill consecutive slots,
-  // and pick the global chunk that belongs in their slot.
-  uint32_t goff[C::kLoads];
-  int gchunk[C::kLoads];
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    const int s = tid + C::kThreads * i;
-    const int row = s >> 3;
-    const int c = (s & 7) ^ ((row >> 1) & 7);
-    const int lrow = row < BN ? row : row - BN;
-    goff[i] = (uint32_t)lrow * (uint32_t)K + (uint32_t)(c << 4);
-    gchunk[i] = c << 4;
-  }
+  // stage hold W, rows BN.. hold A. Lanes of a wave fill consecutive slots
+  // (8 rows of 128 bytes) and pick the global chunk that belongs in their
+  // slot. Slot s holds row (tid >> 3) + 32 i, and its logical chunk
+  // (tid & 7) ^ ((row >> 1) & 7) does not depend on i.
+  const int lchunk = ((tid & 7) ^ ((tid >> 4) & 7)) << 4;
+  const uint32_t lbase = (uint32_t)(tid >> 3) * (uint32_t)K + (uint32_t)lchunk;
+  constexpr int kLoadsW = BN / 32;
   auto issue = [&](int stage, int k0) {
     uint8_t* base = smem + stage * C::kStage;
+    const bool kin = k0 + lchunk < K;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int s0 = wave * 64 + C::kThreads * i;  // first slot of this wave's 64
-      const bool isW = (s0 >> 3) < BN;              // a wave's 8 rows lie on one side
-      const uint32_t off = (k0 + gchunk[i] < K) ? goff[i] + (uint32_t)k0 : kOutOfRange;
-      if (isW) buffer_load16_lds(rW, base + s0 * 16, off);
-      else     buffer_load16_lds(rA, base + s0 * 16, off);
+      const int ii = i < kLoadsW ? i : i - kLoadsW;
+      const uint32_t off = kin ? lbase + (uint32_t)(32 * ii) * (uint32_t)K + (uint32_t)k0 : kOutOfRange;
+      if (i < kLoadsW) buffer_load16_lds(rW, base + s0 * 16, off);
+      else             buffer_load16_lds(rA, base + s0 * 16, off);
     }
   };
 

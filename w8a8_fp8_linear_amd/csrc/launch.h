@@ -16,16 +16,33 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                        uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
-// Routed-expert pipeline (moe.hip).
-size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+// Routed-expert pipeline (moe.hip). offsets/perm are device arrays made by
+// launch_route; the grouped kernels derive their tiles from them on device.
 size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+size_t grouped_gate_up_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int32_t* counts,
                         int32_t* offsets, int32_t* perm, void* scratch, hipStream_t stream);
 
+hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const int32_t* perm,
+                                       const int32_t* offsets, const uint8_t* w13, const float* s13,
+                                       uint16_t* gu, int64_t T, int64_t H, int64_t I, int64_t E,
+                                       int64_t topk, hipStream_t stream);
+
+hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
+                                       const int32_t* offsets, const uint8_t* w13, const float* s13,
+                                       uint8_t* qh, float* sh, int64_t T, int64_t H, int64_t I,
+                                       int64_t E, int64_t topk, hipStream_t stream);
+
+hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
+                               const int32_t* offsets, const float* tw, const uint8_t* w2,
+                               const float* s2, uint16_t* out, float* acc, int64_t T, int64_t H,
+                               int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids,
-                                  const uint8_t* w13, const float* s13, uint16_t* gu,
-                                  int32_t* perm, int64_t T, int64_t H, int64_t I, int64_t E,
+                                  const uint8_t* w13, const float* s13, uint16_t* gu, int32_t* perm,
+                                  int32_t* offsets, int64_t T, int64_t H, int64_t I, int64_t E,
                                   int64_t topk, void* ws, hipStream_t stream);
 
 hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, const float* tw,
