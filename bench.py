@@ -147,6 +147,127 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
     return out
 
 
+def _events(n):
+    import torch
+
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def _avg_ms(evs):
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+
+def _moe_inputs(cfg):
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    d = synth.moe_workload(**cfg, seed=0)
+    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+    x = _bf16_dev(d["x"])
+    q13, s13 = w8.quantize_weight(_bf16_dev(d["w13"].reshape(E * 2 * I, H)))
+    q2, s2 = w8.quantize_weight(_bf16_dev(d["w2"].reshape(E * H, I)))
+    routes = [(torch.from_numpy(i).cuda(), torch.from_numpy(w).cuda()) for i, w in d["routes"]]
+    return x, q13.view(E, 2 * I, H), s13.view(E, 2 * I), q2.view(E, H, I), s2.view(E, H), routes
+
+
+def bench_moe_gate_up(reps=20, warmup=5):
+    """Routed gate/up grouped GEMM, 4096 tokens, top-8 of 64 experts, BF16 result."""
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    cfg = synth.MOE_GATE_UP
+    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+    x, q13, s13, _, _, routes = _moe_inputs(cfg)
+    xq, xs = w8.quantize_per_token(x)
+    ids = routes[0][0]
+    for _ in range(warmup):
+        w8.w8a8_grouped_gemm(xq, xs, ids, q13, s13)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = _events(reps)
+    for a, b in evs:
+        a.record(stream)
+        w8.w8a8_grouped_gemm(xq, xs, ids, q13, s13)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = _avg_ms(evs)
+    flops = 2.0 * T * k * 2 * I * H
+    active = int(torch.unique(ids).numel())
+    bytes_ = active * 2 * I * H + E * 2 * I * 4 + T * H + T * 4 + T * k * 4 + T * k * 2 * I * 2
+    return {"workload": "routed gate/up grouped GEMM, 4096 tokens, H 2048, 64 experts top-8, [1024 x 2048] per expert",
+            "us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_fp8_peak": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+            "algorithmic_bytes": bytes_, "GBs_algorithmic": bytes_ / (ms * 1e-3) / 1e9,
+            "roofline_us": max(flops / (FP8_PEAK_TFLOPS * 1e12), bytes_ / (HBM_PEAK_GBS * 1e9)) * 1e6,
+            "tokens_per_s": T / (ms * 1e-3)}
+
+
+def bench_moe_two_pass(reps=5, warmup=2):
+    """Full routed-expert FFN, 16384 tokens, run twice with the same weights."""
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    cfg = synth.MOE_TWO_PASS
+    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+    x, q13, s13, q2, s2, routes = _moe_inputs(cfg)
+    ws = w8.moe_workspace(T, H, I, E, k)
+    for _ in range(warmup):
+        w8.moe_ffn(x, routes, q13, s13, q2, s2, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = _events(reps)
+    for a, b in evs:
+        a.record(stream)
+        w8.moe_ffn(x, routes, q13, s13, q2, s2, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = _avg_ms(evs)
+    flops_pass = 2.0 * T * k * 2 * I * H + 2.0 * T * k * H * I
+    flops = 2 * flops_pass
+    # per-stage split of one pass, each stage timed on its own
+    xq, xs = w8.quantize_per_token(x)
+    ids, tw = routes[0]
+    stages = {}
+    for name, fn in (
+        ("quantize", lambda: w8.quantize_per_token(x, xq, xs)),
+        ("route", lambda: w8.moe_route(ids, E)),
+    ):
+        ev = _events(reps)
+        for a, b in ev:
+            a.record(stream); fn(); b.record(stream)
+        torch.cuda.synchronize()
+        stages[name] = 1e3 * _avg_ms(ev)
+    counts, offsets, perm = w8.moe_route(ids, E)
+    hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm, offsets, q13, s13, k)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    for name, fn, fl in (
+        ("gate_up_swiglu_quant", lambda: w8.moe_gate_up_swiglu_quant(xq, xs, perm, offsets, q13, s13, k),
+         2.0 * T * k * 2 * I * H),
+        ("down_combine", lambda: w8.moe_down_combine(hq, hs, perm, offsets, tw, q2, s2, out=out, acc=acc),
+         2.0 * T * k * H * I),
+    ):
+        ev = _events(reps)
+        for a, b in ev:
+            a.record(stream); fn(); b.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * _avg_ms(ev)
+        stages[name] = us
+        stages[name + "_tflops"] = fl / (us * 1e-6) / 1e12
+    return {"workload": "routed-expert FFN x2 passes, 16384 tokens, H 2048, I 512, 64 experts top-8, SwiGLU, "
+                        "per-slot requant, weighted combine",
+            "us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_fp8_peak": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, "flops": flops,
+            "roofline_us": flops / (FP8_PEAK_TFLOPS * 1e12) * 1e6,
+            "tokens_per_s": T / (ms * 1e-3), "stage_us_one_pass": stages}
+
+
 def cpu_baseline():
     """The CPU oracle on the full prefill workload (activation quantisation,
     exact float64 GEMM, BF16 rounding), timed once on this host."""
@@ -181,6 +302,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-moe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path does not shard).",
@@ -198,6 +320,12 @@ def main():
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         dec = bench_decode()
+    moe_gu = moe_ffn = None
+    if not args.no_moe:
+        print("[bench] routed gate/up", file=sys.stderr, flush=True)
+        moe_gu = bench_moe_gate_up()
+        print("[bench] routed FFN, two passes", file=sys.stderr, flush=True)
+        moe_ffn = bench_moe_two_pass()
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -227,6 +355,8 @@ def main():
         "quant_GBs": round(pre["quant_gbs"], 1),
         "tokens_per_s": round(pre["tokens_per_s"], 1),
         "decode": dec,
+        "moe_gate_up": moe_gu,
+        "moe_two_pass": moe_ffn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

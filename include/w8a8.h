@@ -16,8 +16,8 @@
  *          Lernex/Metis-1.6-Praxis-NVFP4, hub sidebar): bias 7, largest
  *          magnitude 448, no infinities, NaN = 0x7F / 0xFF.
  *   scale  float32.
- *   All matrices are dense and row-major. Weights are [out, in] with one
- *   scale per output row (Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4").
+ *   All matrices are dense and row-major. Weights are [out, in], each output
+ *   row with its own scale (Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4").
  *
  * Conventions shared by every call
  *   Pointers     Device pointers owned by the caller. The library allocates

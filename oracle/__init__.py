@@ -13,8 +13,8 @@ What it defines, and where the pages state it:
 * Per-row dynamic quantisation (``quant``): one scale per token for
   activations and one per output row for weights (Lernex/Metis-1.6-Logos-
   FP8, "What is in FP8"; sglang-metis 0.1.0, "Serve", memory paragraph).
-* The W8A8 linear (``linear``): each layer's input rounded to FP8 per token
-  and multiplied with the FP8 weights (Lernex/Metis-1.6-Logos-FP8, "What
+* The W8A8 linear (``linear``): the per-token FP8 version of a layer's
+  input times the FP8 weights (Lernex/Metis-1.6-Logos-FP8, "What
   --fast-math does"); the weights are decoded exactly and the product is
   carried out in high precision, the emulation the same page's
   "Benchmarks" section describes for its FP8 scores.

@@ -1,10 +1,11 @@
 """The W8A8 linear layer of the oracle — test infrastructure only.
 
 What the layer computes (Lernex/Metis-1.6-Logos-FP8, "What --fast-math
-does"): the layer's input, rounded to FP8 per token, is multiplied with the
-FP8 weights. The same page's "Benchmarks" section scores the FP8 model by
-decoding the stored weights exactly and running them with every quantised
-layer's input rounded to FP8 per token; that emulation is this oracle:
+does"): the input is converted to FP8 with a scale per token and the
+product with the FP8 weights is formed. The same page's "Benchmarks"
+section evaluates the FP8 model by decoding the stored weights exactly and
+feeding every quantised layer a per-token FP8 version of its input; that
+emulation is this oracle:
 
     Y[m, n] = bf16( s_x[m] * s_w[n] * sum_k dec(qx[m, k]) * dec(qw[n, k]) )
 

@@ -7,8 +7,8 @@ other.
 
 Workloads (shapes and value distributions) follow the dense projection and
 routed-expert settings that the Metis-1.6 pages describe: activations are
-per-token BF16 rows, weights are [out, in] rows with one scale per output
-row (Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4"; Lernex/Metis-1.6-
+per-token BF16 rows, weights are [out, in] rows with a scale for each
+output row (Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4"; Lernex/Metis-1.6-
 Logos-FP8, "What is in FP8"), the routed experts are stored in global
 expert order and each token picks the top-k of them (Lernex/Metis-1.6-
 Praxis, "Architecture").

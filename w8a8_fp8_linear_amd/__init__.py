@@ -306,9 +306,9 @@ def moe_w8a8_grouped(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_
 
 def moe_ffn(x, routes, w13_q, w13_scale, w2_q, w2_scale, workspace=None):
     """The routed-expert stage run once per entry of ``routes`` with the same
-    weights, each pass fed the previous pass's BF16 output (the stack runs
-    twice per token with shared weights; sglang-metis 0.1.0, "How the model
-    maps onto SGLang"). ``routes`` is a list of (topk_ids, topk_w). Returns the
+    weights, each pass fed the previous pass's BF16 output (every token goes
+    through the block stack two times on one set of weights; sglang-metis
+    0.1.0, "How the model maps onto SGLang"). ``routes`` is a list of (topk_ids, topk_w). Returns the
     list of per-pass BF16 outputs."""
     outs = []
     for ids, w in routes:

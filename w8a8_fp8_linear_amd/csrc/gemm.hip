@@ -1,9 +1,9 @@
 // Scaled FP8 GEMM: Y[m, n] = bf16( sa[m] * sw[n] * sum_k dec(A[m, k]) * dec(W[n, k]) ).
 //
-// This is the multiply the pages' fast-math path performs: each layer's
-// input rounded to FP8 per token and multiplied with the FP8 weights on the
-// FP8 matrix units (Lernex/Metis-1.6-Logos-FP8, "What --fast-math does"),
-// weights stored [out, in] with one scale per output row (Lernex/Metis-1.6-
+// This is the multiply of the pages' fast-math path: the per-token FP8
+// version of a layer's input times the FP8 weights, computed on the FP8
+// matrix units (Lernex/Metis-1.6-Logos-FP8, "What --fast-math does"),
+// weights stored [out, in], each output row with its own scale (Lernex/Metis-1.6-
 // Praxis-NVFP4, "What is in NVFP4"). Both operands are K-contiguous.
 //
 // Two kernels:
@@ -15,9 +15,9 @@
 //    both scales in fp32, rounds to BF16 and goes through LDS so that every
 //    global store is a full 16-byte row segment. Workgroup ids are renumbered
 //    so that each of the 8 XCDs walks a compact block of tiles (its own L2).
-//  * gemm_skinny: at most 32 tokens (decode). The time is the weight stream
-//    (the pages: that step is set by how fast the GPU reads the weights;
-//    "What --fast-math does"). A workgroup owns 16 weight rows, its 4 waves
+//  * gemm_skinny: at most 32 tokens (decode). The time is the weight stream:
+//    the pages note that single-stream generation is limited by weight
+//    bandwidth rather than arithmetic ("What --fast-math does"). A workgroup owns 16 weight rows, its 4 waves
 //    split K, each lane loads its MFMA operands straight from global memory
 //    with 16-byte loads (every weight byte is read once), and the partial
 //    sums meet in LDS.

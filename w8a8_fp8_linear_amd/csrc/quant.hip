@@ -1,8 +1,8 @@
 // Per-row dynamic FP8 quantisation (activations per token, weights per
 // output row).
 //
-// The pages quantise activations per token at run time and weights with one
-// scale per output channel (Lernex/Metis-1.6-Logos-FP8, "What is in FP8";
+// The pages quantise activations per token at run time and give the
+// weights a scale for each output channel (Lernex/Metis-1.6-Logos-FP8, "What is in FP8";
 // Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4": one scale per output
 // row). For a row x: amax = max|x| (exact, on the BF16 bit patterns),
 // s = fl32(amax / 448) (s = 1 for an all-zero row), q = E4M3(fl32(x / s))
