@@ -236,21 +236,26 @@ def bench_moe_two_pass(reps=5, warmup=2):
     stages = {}
     for name, fn in (
         ("quantize", lambda: w8.quantize_per_token(x, xq, xs)),
-        ("route", lambda: w8.moe_route(ids, E)),
+        ("route_both_orders", lambda: (w8.moe_route(ids, E, order=0),
+                                       w8.moe_route(ids, E, order=1, with_slot_row=True))),
     ):
         ev = _events(reps)
         for a, b in ev:
             a.record(stream); fn(); b.record(stream)
         torch.cuda.synchronize()
         stages[name] = 1e3 * _avg_ms(ev)
-    counts, offsets, perm = w8.moe_route(ids, E)
-    hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm, offsets, q13, s13, k)
+    _, off0, perm0 = w8.moe_route(ids, E, order=0)
+    _, off1, perm1, row1 = w8.moe_route(ids, E, order=1, with_slot_row=True)
+    gu_ws = torch.empty(int(w8.lib().moe_gate_up_swiglu_quant_workspace_bytes(T, I, k)), dtype=torch.uint8,
+                        device="cuda")
+    hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0, dst_row=row1, workspace=gu_ws)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
     for name, fn, fl in (
-        ("gate_up_swiglu_quant", lambda: w8.moe_gate_up_swiglu_quant(xq, xs, perm, offsets, q13, s13, k),
+        ("gate_up_swiglu_quant", lambda: w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0,
+                                                                     dst_row=row1, workspace=gu_ws),
          2.0 * T * k * 2 * I * H),
-        ("down_combine", lambda: w8.moe_down_combine(hq, hs, perm, offsets, tw, q2, s2, out=out, acc=acc),
+        ("down_combine", lambda: w8.moe_down_combine(hq, hs, perm1, off1, tw, q2, s2, out=out, acc=acc),
          2.0 * T * k * H * I),
     ):
         ev = _events(reps)
@@ -303,6 +308,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path does not shard).",
@@ -314,6 +321,12 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] prefill: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     pre = bench_prefill(args.steps, args.warmup)
     dec = None
@@ -346,7 +359,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations with 1% x20 outlier channels, N(0,0.02) weights)",
         "config": {"workload": "prefill projection 4096 tokens x 2048 -> 6144 (per-token quant + W8A8 GEMM)",
                    "M": pre["M"], "N": pre["N"], "K": pre["K"]},
-        "roofline": {"bound": "mfma", "kernel": "gemm_tiled<256,192>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_tiled<256,192,2,4>", "achieved": round(achieved, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": None},
         "gemm_us_avg": round(pre["gemm_ms_avg"] * 1e3, 3),

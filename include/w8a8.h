@@ -137,39 +137,56 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
  *   w13_scale[E, 2I]      float32 per output row
  *   w2_q     [E, H, I]    E4M3
  *   w2_scale [E, H]       float32 per output row
- * A slot is the flat index t * topk + j. The expert-sorted order lists the
- * valid slots grouped by expert id, increasing slot index inside an expert.
- * Limits: 1 <= E <= 1024, 1 <= topk <= 64, H and I positive multiples of 16,
- * T * topk, T * H and 2 * I * H below 2^31. The fused calls need I = 256 or
- * 512. T == 0 is a no-op. offsets/perm passed to the stage calls must come
+ * A slot is the flat index t * topk + j. Two sorted orders of the valid
+ * slots exist, both stable (increasing slot index inside a group):
+ *   order 0, expert-major:        E groups, group of slot = its expert id e;
+ *   order 1, slot-position-major: topk * E groups, group = j * E + e.
+ * The down projection uses order 1: it runs once per top-k position j, each
+ * token occurs once per run, and the k terms of a token are accumulated
+ * without atomics in the fixed order j = 0..k-1. The gate/up tiles use
+ * order 0, whose groups are k times larger (less padding in partial tiles).
+ * Limits: 1 <= E <= 1024, 1 <= topk <= 64, at most 1024 routing groups
+ * (E, or topk * E in order 1), H and I positive multiples of 16,
+ * T * topk, T * H and 2 * I * H below 2^31. The fused calls need I to be a
+ * multiple of 128. T == 0 is a no-op. offsets/perm passed to the stage calls must come
  * from moe_route (they are read on the device, never on the host).
  * ------------------------------------------------------------------------- */
 
 /* Bytes of scratch moe_route needs (0 for invalid sizes). */
-size_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+size_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E, int order);
 
 /*
- * moe_route — expert-sorted permutation of the routed slots.
- *   counts  [E]       number of valid slots per expert
- *   offsets [E + 1]   exclusive prefix of counts; offsets[E] = valid slots
- *   perm    [T*topk]  perm[offsets[e] + i] = i-th slot (increasing) routed
- *                     to e; entries from offsets[E] on are set to -1
+ * moe_route — sorted permutation of the routed slots (order 0 or 1, above).
+ * With G groups (G = E for order 0, topk * E for order 1):
+ *   counts  [G]       number of valid slots per group
+ *   offsets [G + 1]   exclusive prefix of counts; offsets[G] = valid slots
+ *   perm    [T*topk]  perm[offsets[g] + i] = i-th slot (increasing) of group
+ *                     g; entries from offsets[G] on are set to -1
+ *   slot_row [T*topk] optional (NULL = not written): the inverse map,
+ *                     slot_row[perm[r]] = r, and -1 for a slot whose id is
+ *                     dropped
  *   workspace         device scratch of moe_route_workspace_bytes bytes
  * Bit-exact, deterministic. Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED,
  * MISALIGNED, WORKSPACE, DEVICE, LAUNCH.
  */
-int moe_route(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* counts, int32_t* offsets,
-              int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int moe_route(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int order, int32_t* counts,
+              int32_t* offsets, int32_t* perm, int32_t* slot_row, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
 
 /*
  * moe_gate_up_bf16 — grouped gate/up projection, BF16 result.
  *   gu_bf16[r, :] = bf16( x_scale[t] * w13_scale[e, :] * (x_q[t, :] . w13_q[e]^T) )
  * for the r-th sorted slot (t = perm[r] / topk, e its expert); gu_bf16 is
- * [T*topk, 2I], rows from offsets[E] on are left untouched.
+ * [T*topk, 2I], rows from offsets[G] on are left untouched. `order` is the
+ * order perm/offsets were made with.
  */
 int moe_gate_up_bf16(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
                      const uint8_t* w13_q, const float* w13_scale, uint16_t* gu_bf16, int64_t T, int64_t H,
-                     int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+                     int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+/* Bytes of scratch moe_gate_up_swiglu_quant needs: T*topk*(4 I + 4) rounded
+ * up (0 for invalid sizes). */
+size_t moe_gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk);
 
 /*
  * moe_gate_up_swiglu_quant — grouped gate/up projection with the expert
@@ -178,19 +195,26 @@ int moe_gate_up_bf16(const uint8_t* x_q, const float* x_scale, const int32_t* pe
  *   h    = silu(g) * u                       (float32)
  *   h_scale[r] = fl32(max|h| / 448) (1 if h == 0),
  *   h_q[r, i]  = E4M3(fl32(h[i] / h_scale[r]))  (round to nearest even, saturating)
- *   h_q [T*topk, I], h_scale [T*topk], both in sorted order. I = 256 or 512.
+ * h_q [T*topk, I] and h_scale [T*topk]. The row r a slot's h goes to is its
+ * sorted row under perm, or dst_row[slot] when dst_row is given (a
+ * slot_row array of moe_route in the other order: the tiles then follow
+ * `perm`, the output rows the other order). Rows from offsets[G] on are left
+ * untouched. I must be a multiple of 128. `order` is the order perm/offsets
+ * were made with. The workspace holds the float32 h rows and their maxima.
  */
 int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
-                             const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q, float* h_scale, int64_t T,
-                             int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+                             const int32_t* dst_row, const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q,
+                             float* h_scale, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_down_combine — grouped down projection and router-weighted combine:
  *   y[r, :]      = h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T)
  *   out_bf16[t]  = bf16( sum over the token's valid slots of topk_w[slot] * y )
- * Sums are float32 (atomic, so their order, and the last bit of a sum, can
- * vary between runs). acc_f32 [T, H] is caller-provided scratch; it is
- * cleared by the call. A token with no valid slot gets zeros.
+ * perm/offsets must be in order 1 (slot-position-major). The sum is float32,
+ * taken in the order j = 0..topk-1 (deterministic). acc_f32 [T, H] is
+ * caller-provided scratch; it is cleared by the call. A token with no valid
+ * slot gets zeros.
  */
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
                      const float* topk_w, const uint8_t* w2_q, const float* w2_scale, uint16_t* out_bf16,
@@ -214,10 +238,13 @@ int w8a8_grouped_gemm(const uint8_t* x_q, const float* x_scale, const int32_t* t
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 
 /*
- * moe_w8a8_grouped — one routed-expert pass: moe_route, then
- * moe_gate_up_swiglu_quant, then moe_down_combine, on buffers carved from
- * `workspace`. out_bf16 [T, H]. Running the stack's two passes is two calls,
- * the second on quantize_per_token of the first call's output.
+ * moe_w8a8_grouped — one routed-expert pass on buffers carved from
+ * `workspace`: moe_route in both orders, moe_gate_up_swiglu_quant with
+ * order-0 tiles writing each h row at its order-1 row (dst_row = the
+ * order-1 slot_row), then moe_down_combine on the order-1 arrays.
+ * out_bf16 [T, H]. I must be a multiple of 128. Running the stack's two
+ * passes is two calls, the second on quantize_per_token of the first
+ * call's output.
  */
 int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const float* topk_w,
                      const uint8_t* w13_q, const float* w13_scale, const uint8_t* w2_q, const float* w2_scale,

@@ -29,6 +29,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 import w8a8_fp8_linear_amd as w8  # noqa: E402
 
 SMALL = dict(T=37, H=256, I=256, E=5, k=3, n_outlier=2)
+RAGGED = dict(T=301, H=272, I=384, E=9, k=4, n_outlier=3)   # K tail, 3 gate/up tiles, odd groups
 GATE_UP = dict(T=4096, H=2048, I=512, E=64, k=8, n_outlier=20)
 TWO_PASS = dict(T=16384, H=2048, I=512, E=64, k=8, n_outlier=20, passes=2)
 
@@ -42,6 +43,11 @@ def small():
     ids[10, 0] = SMALL["E"]
     d["routes"][0] = (ids, w)
     return d
+
+
+@pytest.fixture(scope="module")
+def ragged():
+    return quantized_moe(**RAGGED, seed=11)
 
 
 @pytest.fixture(scope="module")
@@ -59,23 +65,43 @@ def _dev(d):
             "q2": to_dev(d["q2"]), "s2": to_dev(d["s2"])}
 
 
+def slot_position_ids(ids, E):
+    """Group keys of the slot-position-major order: j * E + e (invalid ids stay invalid)."""
+    ids = np.asarray(ids)
+    j = np.arange(ids.shape[1])[None, :]
+    return np.where((ids >= 0) & (ids < E), j * E + ids, -1).astype(np.int32)
+
+
+def oracle_route(ids, E, order):
+    if order == 0:
+        return oracle.route(ids, E)
+    return oracle.route(slot_position_ids(ids, E), ids.shape[1] * E)
+
+
+@pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (37, 3, 5), (1000, 8, 7), (4096, 8, 64), (16384, 8, 64),
                                    (513, 4, 130), (2000, 2, 1024)])
-def test_route_bitexact(T, k, E):
-    print(f"[route] T={T} k={k} E={E}", flush=True)
+def test_route_bitexact(T, k, E, order):
+    if order == 1 and k * E > 1024:
+        pytest.skip("more than 1024 routing groups")
+    print(f"[route] T={T} k={k} E={E} order={order}", flush=True)
     rng = np.random.default_rng(T + k + E)
     ids = rng.integers(-1, E + 1, (T, k)).astype(np.int32)
     if E == 64:
         from synth import routing
         ids, _ = routing(rng, T, E, k)
-    counts, offsets, perm = w8.moe_route(to_dev(ids), E)
+    counts, offsets, perm, slot_row = w8.moe_route(to_dev(ids), E, order, with_slot_row=True)
     torch.cuda.synchronize()
-    rc, ro, rp = oracle.route(ids, E)
+    rc, ro, rp = oracle_route(ids, E, order)
     assert np.array_equal(counts.cpu().numpy(), rc)
     assert np.array_equal(offsets.cpu().numpy(), ro)
     p = perm.cpu().numpy()
     assert np.array_equal(p[:rp.size], rp)
     assert np.all(p[rp.size:] == -1)
+    # slot_row is the inverse permutation, -1 on dropped slots
+    want = np.full(T * k, -1, np.int64)
+    want[rp] = np.arange(rp.size)
+    assert np.array_equal(slot_row.cpu().numpy(), want)
 
 
 def test_route_deterministic():
@@ -114,24 +140,42 @@ def test_gate_up_bf16_full_size(gate_up_cfg):
     _check_gate_up_bf16(gate_up_cfg)
 
 
-def _check_fused_requant(d, route_idx=0, sample=None):
+def _check_fused_requant(d, route_idx=0, sample=None, tile_order=0):
+    """h rows land in the position-major (order 1) order; the tiles follow
+    `tile_order` (0: expert-major tiles writing through dst_row, as the full
+    pass does; 1: position-major tiles, rows in place)."""
     dv = _dev(d)
     ids, _ = d["routes"][route_idx]
-    counts, offsets, perm = w8.moe_route(to_dev(ids), d["E"])
-    hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, offsets, dv["q13"], dv["s13"], d["k"])
+    counts, offsets, perm, row1 = w8.moe_route(to_dev(ids), d["E"], order=1, with_slot_row=True)
+    if tile_order == 0:
+        _, off0, perm0 = w8.moe_route(to_dev(ids), d["E"], order=0)
+        hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm0, off0, dv["q13"], dv["s13"], d["k"],
+                                             order=0, dst_row=row1)
+    else:
+        hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, offsets, dv["q13"], dv["s13"], d["k"],
+                                             order=1)
     torch.cuda.synchronize()
-    _, _, rp = oracle.route(ids, d["E"])
+    _, _, rp = oracle_route(ids, d["E"], 1)
+    assert np.array_equal(perm.cpu().numpy()[:rp.size], rp)
     rows = np.arange(rp.size) if sample is None else np.sort(
         np.random.default_rng(1).choice(rp.size, min(sample, rp.size), replace=False))
     gu64, err = sorted_rows_gate_up(d["qx"], d["sx"], ids, rp, rows, d["q13"], d["s13"], d["k"])
     rep = check_requant(hq.cpu().numpy()[rows], hs.cpu().numpy()[rows], gu64, err)
     print("fused requant", rep, flush=True)
-    record(f"moe fused swiglu+requant T={d['T']} E={d['E']} k={d['k']} rows={len(rows)}", rep)
+    record(f"moe fused swiglu+requant T={d['T']} E={d['E']} k={d['k']} I={d['I']} tiles=order{tile_order} "
+           f"rows={len(rows)}", rep)
     return hq, hs, perm, offsets
 
 
-def test_fused_requant_small(small):
-    _check_fused_requant(small)
+@pytest.mark.parametrize("tile_order", [0, 1])
+def test_fused_requant_small(small, tile_order):
+    _check_fused_requant(small, tile_order=tile_order)
+
+
+@pytest.mark.parametrize("tile_order", [0, 1])
+def test_fused_requant_ragged(ragged, tile_order):
+    """I = 384 (three 128-column h tiles), H = 272 (a 16-byte K tail), 9 experts."""
+    _check_fused_requant(ragged, tile_order=tile_order)
 
 
 def test_fused_requant_gate_up_cfg(gate_up_cfg):
@@ -160,6 +204,22 @@ def test_down_combine_small(small):
     _check_down(small, hq, hs, perm, offsets)
 
 
+def test_down_combine_ragged(ragged):
+    hq, hs, perm, offsets = _check_fused_requant(ragged)
+    _check_down(ragged, hq, hs, perm, offsets)
+
+
+def test_down_combine_deterministic(small):
+    dv = _dev(small)
+    ids, tw = small["routes"][0]
+    _, offsets, perm = w8.moe_route(to_dev(ids), small["E"], order=1)
+    hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, offsets, dv["q13"], dv["s13"], small["k"],
+                                         order=1)
+    outs = [bf16_bits(w8.moe_down_combine(hq, hs, perm, offsets, to_dev(tw), dv["q2"], dv["s2"])) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
 def test_down_combine_two_pass_cfg(two_pass_cfg):
     hq, hs, perm, offsets = _check_fused_requant(two_pass_cfg, sample=4096)
     _check_down(two_pass_cfg, hq, hs, perm, offsets, n_tokens=512)
@@ -171,15 +231,17 @@ def _oracle_pass_tokens(qx, sx, ids, w, d, tokens):
     return out64
 
 
-def test_full_pass_small(small):
-    dv = _dev(small)
-    ids, w = small["routes"][0]
+@pytest.mark.parametrize("cfg", ["small", "ragged"])
+def test_full_pass_small(cfg, request):
+    d = request.getfixturevalue(cfg)
+    dv = _dev(d)
+    ids, w = d["routes"][0]
     out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
     torch.cuda.synchronize()
-    ref64 = _oracle_pass_tokens(small["qx"], small["sx"], ids, w, small, np.arange(small["T"]))
+    ref64 = _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, np.arange(d["T"]))
     rep = bf16_compare(bf16_bits(out), ref64)
-    print("full pass small", rep, flush=True)
-    record("moe full pass small", rep)
+    print(f"full pass {cfg}", rep, flush=True)
+    record(f"moe full pass {cfg} T={d['T']} H={d['H']} I={d['I']} E={d['E']} k={d['k']}", rep)
     assert rep["frobenius"] <= 4e-3, rep
 
 
@@ -235,3 +297,17 @@ def test_moe_argument_errors(small):
     with pytest.raises(w8.W8A8Error) as e:
         w8.moe_w8a8_grouped(dv["qx"], dv["sx"], ids, w, q13, s13, q2, s2)   # I = 48 has no fused kernel
     assert e.value.status == 4
+
+
+def test_mismatched_order_is_rejected(small):
+    """Offsets made in one sorted order cannot be handed to a stage expecting
+    the other: the binding checks their length before anything is launched."""
+    dv = _dev(small)
+    ids, tw = small["routes"][0]
+    _, off0, perm0 = w8.moe_route(to_dev(ids), small["E"], order=0)
+    with pytest.raises(ValueError):
+        w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm0, off0, dv["q13"], dv["s13"], small["k"], order=1)
+    hq = torch.zeros((small["T"] * small["k"], small["I"]), dtype=torch.uint8, device="cuda")
+    hs = torch.ones(small["T"] * small["k"], dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        w8.moe_down_combine(hq, hs, perm0, off0, to_dev(tw), dv["q2"], dv["s2"])

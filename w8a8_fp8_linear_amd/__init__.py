@@ -35,11 +35,13 @@ _SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quantize_per_token": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "w8a8_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
-    "moe_route_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
-    "moe_route": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
-                                 _c_ptr]),
-    "moe_gate_up_bf16": (ctypes.c_int, [_c_ptr] * 7 + [_c_i64] * 5 + [_c_ptr]),
-    "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr]),
+    "moe_route_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, ctypes.c_int]),
+    "moe_route": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                 _c_ptr, ctypes.c_size_t, _c_ptr]),
+    "moe_gate_up_bf16": (ctypes.c_int, [_c_ptr] * 7 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
+    "moe_gate_up_swiglu_quant_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 3),
+    "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr, ctypes.c_size_t,
+                                                                          _c_ptr]),
     "moe_down_combine": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [_c_ptr]),
     "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "w8a8_grouped_gemm": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
@@ -179,6 +181,16 @@ def w8a8_linear(x, w_q, w_scale, out=None):
 # "sorted" arrays list the valid slots grouped by expert (stable).
 
 
+def _check_order(offsets, E: int, topk: int, order: int) -> None:
+    """The grouped kernels walk offsets on the device; its length must match the order."""
+    want = (topk * E if order else E) + 1
+    if order not in (0, 1):
+        raise ValueError("order must be 0 (expert-major) or 1 (slot-position-major)")
+    if offsets.numel() != want:
+        raise ValueError(f"offsets has {offsets.numel()} entries; order {order} with E={E}, topk={topk} "
+                         f"needs {want} (route with moe_route(..., order={order}))")
+
+
 def _moe_dims(x_q, topk_ids, w13_q):
     T, H = x_q.shape
     E, twoI, H2 = w13_q.shape
@@ -189,57 +201,86 @@ def _moe_dims(x_q, topk_ids, w13_q):
     return T, H, twoI // 2, E, topk_ids.shape[1]
 
 
-def moe_route(topk_ids, E: int):
-    """Expert-sorted order of the routed slots: (counts [E], offsets [E+1], perm [T*k]) int32."""
+def moe_route(topk_ids, E: int, order: int = 0, with_slot_row: bool = False):
+    """Sorted order of the routed slots: (counts [G], offsets [G+1], perm [T*k]) int32,
+    plus slot_row [T*k] (slot -> sorted row, -1 if dropped) when ``with_slot_row``.
+
+    order 0: G = E groups by expert; order 1: G = k * E groups keyed
+    j * E + e (slot position j, expert e), the order the down projection uses.
+    """
     import torch
 
     _want(topk_ids, torch.int32, 2, "topk_ids")
     T, k = topk_ids.shape
+    G = k * E if order else E
     dev = topk_ids.device
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    counts = torch.empty(G, dtype=torch.int32, device=dev)
+    offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
-    nbytes = max(int(lib().moe_route_workspace_bytes(T, k, E)), 16)
+    slot_row = torch.empty(T * k, dtype=torch.int32, device=dev) if with_slot_row else None
+    nbytes = max(int(lib().moe_route_workspace_bytes(T, k, E, order)), 16)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    _check("moe_route", lib().moe_route(topk_ids.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
-                                        perm.data_ptr(), ws.data_ptr(), nbytes, _stream(topk_ids)))
+    _check("moe_route", lib().moe_route(topk_ids.data_ptr(), T, k, E, order, counts.data_ptr(), offsets.data_ptr(),
+                                        perm.data_ptr(), slot_row.data_ptr() if with_slot_row else None,
+                                        ws.data_ptr(), nbytes, _stream(topk_ids)))
+    if with_slot_row:
+        return counts, offsets, perm, slot_row
     return counts, offsets, perm
 
 
-def moe_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int):
-    """Sorted-slot gate/up rows in BF16: [T*k, 2I]."""
+def moe_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int, order: int = 0):
+    """Sorted-slot gate/up rows in BF16: [T*k, 2I] (perm/offsets made with ``order``)."""
     import torch
 
     T, H = x_q.shape
     E, twoI, _ = w13_q.shape
+    _check_order(offsets, E, topk, order)
     gu = torch.empty((T * topk, twoI), dtype=torch.bfloat16, device=x_q.device)
     _check("moe_gate_up_bf16", lib().moe_gate_up_bf16(
         x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), w13_q.data_ptr(),
-        w13_scale.data_ptr(), gu.data_ptr(), T, H, twoI // 2, E, topk, _stream(x_q)))
+        w13_scale.data_ptr(), gu.data_ptr(), T, H, twoI // 2, E, topk, order, _stream(x_q)))
     return gu
 
 
-def moe_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int):
-    """Sorted-slot requantised h = silu(g) * u: (h_q uint8 [T*k, I], h_scale f32 [T*k])."""
+def moe_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int, order: int = 0,
+                             dst_row=None, workspace=None):
+    """Requantised h = silu(g) * u: (h_q uint8 [T*k, I], h_scale f32 [T*k]).
+
+    The tiles follow perm/offsets (made with ``order``); a slot's h lands on
+    its sorted row, or on ``dst_row[slot]`` when given (the slot_row of a
+    moe_route in the other order)."""
     import torch
 
     T, H = x_q.shape
     E, twoI, _ = w13_q.shape
+    _check_order(offsets, E, topk, order)
     I = twoI // 2
+    if dst_row is not None:
+        _want(dst_row, torch.int32, 1, "dst_row")
+        if dst_row.numel() != T * topk:
+            raise ValueError("dst_row must have T * topk entries")
+    nbytes = max(int(lib().moe_gate_up_swiglu_quant_workspace_bytes(T, I, topk)), 16)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
     h_q = torch.empty((T * topk, I), dtype=torch.uint8, device=x_q.device)
     h_s = torch.empty((T * topk,), dtype=torch.float32, device=x_q.device)
     _check("moe_gate_up_swiglu_quant", lib().moe_gate_up_swiglu_quant(
-        x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), w13_q.data_ptr(),
-        w13_scale.data_ptr(), h_q.data_ptr(), h_s.data_ptr(), T, H, I, E, topk, _stream(x_q)))
+        x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(),
+        dst_row.data_ptr() if dst_row is not None else None, w13_q.data_ptr(), w13_scale.data_ptr(),
+        h_q.data_ptr(), h_s.data_ptr(), T, H, I, E, topk, order, workspace.data_ptr(), workspace.numel(),
+        _stream(x_q)))
     return h_q, h_s
 
 
 def moe_down_combine(h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out=None, acc=None):
-    """Down projection of the sorted slots and the router-weighted combine: BF16 [T, H]."""
+    """Down projection of the sorted slots and the router-weighted combine: BF16 [T, H].
+
+    perm/offsets must come from ``moe_route(..., order=1)``."""
     import torch
 
     T, k = topk_w.shape
     E, H, I = w2_q.shape
+    _check_order(offsets, E, k, 1)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
     if acc is None:

@@ -99,7 +99,9 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
 namespace {
 
 constexpr int64_t kMaxExperts = 1024;
+constexpr int64_t kMaxGroups = 1024;  // routing groups: E, or topk * E in slot-position-major order
 constexpr int64_t kMaxTopk = 64;
+constexpr int64_t kFusedIMultiple = 128;  // a gate/up tile holds 128 h columns (256 weight rows)
 
 // Shared checks of the routed-expert calls. Returns W8A8_OK or a status.
 int check_moe_shape(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
@@ -130,51 +132,67 @@ bool any_null(std::initializer_list<const void*> ps) {
 
 extern "C" {
 
-size_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
-  if (T < 0 || topk < 1 || E < 1 || !mul_ok(T, topk)) return 0;
-  return w8a8::route_workspace_bytes(T, topk, E);
+size_t moe_route_workspace_bytes(int64_t T, int64_t topk, int64_t E, int order) {
+  if (T < 0 || topk < 1 || E < 1 || !mul_ok(T, topk) || (order != 0 && order != 1)) return 0;
+  return w8a8::route_workspace_bytes(T, topk, w8a8::route_groups(topk, E, order));
 }
 
-int moe_route(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* counts, int32_t* offsets,
-              int32_t* perm, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int moe_route(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int order, int32_t* counts,
+              int32_t* offsets, int32_t* perm, int32_t* slot_row, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
   if (T < 0 || topk < 0 || E < 0 || !mul_ok(T, topk)) return W8A8_ERR_BAD_SHAPE;
   if (E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk || T * topk > INT32_MAX) return W8A8_ERR_UNSUPPORTED;
+  if (order != 0 && order != 1) return W8A8_ERR_UNSUPPORTED;
+  if (w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (T == 0) return W8A8_OK;
   if (any_null({topk_ids, counts, offsets, perm, workspace})) return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({topk_ids, counts, offsets, perm, workspace})) return W8A8_ERR_MISALIGNED;
-  if (workspace_bytes < w8a8::route_workspace_bytes(T, topk, E)) return W8A8_ERR_WORKSPACE;
+  if (!all_aligned({topk_ids, counts, offsets, perm, slot_row, workspace})) return W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < w8a8::route_workspace_bytes(T, topk, w8a8::route_groups(topk, E, order)))
+    return W8A8_ERR_WORKSPACE;
   const int d = check_device();
   if (d != W8A8_OK) return d;
-  return launch_status(w8a8::launch_route(topk_ids, T, topk, E, counts, offsets, perm, workspace, stream));
+  return launch_status(
+      w8a8::launch_route(topk_ids, T, topk, E, order, counts, offsets, perm, slot_row, workspace, stream));
 }
 
 int moe_gate_up_bf16(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
                      const uint8_t* w13_q, const float* w13_scale, uint16_t* gu_bf16, int64_t T, int64_t H, int64_t I,
-                     int64_t E, int64_t topk, hipStream_t stream) {
+                     int64_t E, int64_t topk, int order, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
+  if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (T == 0) return W8A8_OK;
   if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16})) return W8A8_ERR_NULL_ARG;
   if (!all_aligned({x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16})) return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(
-      w8a8::launch_grouped_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16, T, H, I, E, topk, stream));
+      w8a8::launch_grouped_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16, T, H, I, E, topk, order,
+                                        stream));
+}
+
+size_t moe_gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk) {
+  if (T < 0 || I < 0 || topk < 1 || !mul_ok(T, topk) || !mul_ok(T * topk, I) || !mul_ok(T * topk * I, 4)) return 0;
+  return w8a8::gate_up_swiglu_quant_workspace_bytes(T, I, topk);
 }
 
 int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
-                             const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q, float* h_scale, int64_t T,
-                             int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
+                             const int32_t* dst_row, const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q,
+                             float* h_scale, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
-  if (I != 256 && I != 512) return W8A8_ERR_UNSUPPORTED;
+  if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
+  if (I % kFusedIMultiple != 0) return W8A8_ERR_UNSUPPORTED;
   if (T == 0) return W8A8_OK;
-  if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale})) return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale})) return W8A8_ERR_MISALIGNED;
+  if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale, workspace})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale, h_q, h_scale, workspace}))
+    return W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < w8a8::gate_up_swiglu_quant_workspace_bytes(T, I, topk)) return W8A8_ERR_WORKSPACE;
   const int d = check_device();
   if (d != W8A8_OK) return d;
-  return launch_status(w8a8::launch_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale,
-                                                         T, H, I, E, topk, stream));
+  return launch_status(w8a8::launch_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale, h_q,
+                                                         h_scale, T, H, I, E, topk, order, workspace, stream));
 }
 
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
@@ -182,6 +200,7 @@ int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* pe
                      float* acc_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
+  if (w8a8::route_groups(topk, E, 1) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (T == 0) return W8A8_OK;
   if (any_null({h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16, acc_f32})) return W8A8_ERR_NULL_ARG;
   if (!all_aligned({h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16, acc_f32}))
@@ -215,7 +234,7 @@ int w8a8_grouped_gemm(const uint8_t* x_q, const float* x_scale, const int32_t* t
 }
 
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
-  if (check_moe_shape(T, H, I, E, topk) != W8A8_OK) return 0;
+  if (check_moe_shape(T, H, I, E, topk) != W8A8_OK || w8a8::route_groups(topk, E, 1) > kMaxGroups) return 0;
   return w8a8::moe_workspace_bytes(T, H, I, E, topk);
 }
 
@@ -225,7 +244,8 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
                      size_t workspace_bytes, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
-  if (I != 256 && I != 512) return W8A8_ERR_UNSUPPORTED;
+  if (I % kFusedIMultiple != 0) return W8A8_ERR_UNSUPPORTED;
+  if (w8a8::route_groups(topk, E, 1) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (T == 0) return W8A8_OK;
   if (any_null({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
     return W8A8_ERR_NULL_ARG;

@@ -113,9 +113,11 @@ __device__ inline void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int&
   tn = within / gsize;
 }
 
-// Byte offset of logical 16-byte chunk c of a staged row. The XOR spreads
-// the 16 rows read by one MFMA operand load over distinct LDS banks.
-__device__ inline int stage_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+// Byte offset of logical 16-byte chunk c of a staged 128-byte row. A
+// ds_read_b128 is served 8 lanes at a time over 128 bytes of banks; the 8
+// lanes of a group read 8 consecutive rows at the same logical chunk, and
+// the XOR with (row & 7) puts them on 8 different 16-byte bank groups.
+__device__ inline int stage_off(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 
 // FP8 x FP8 -> FP32, 32x32 outputs, 64-deep (E4M3 both operands).
 __device__ inline v16f mfma_32x32x64_e4m3(v8i a, v8i b, v16f c) {

@@ -7,11 +7,13 @@
 // Praxis-NVFP4, "What is in NVFP4"). Both operands are K-contiguous.
 //
 // Two kernels:
-//  * gemm_tiled: many tokens (prompt reading). A workgroup of 4 waves owns a
-//    BM x BN output tile. Each 128-deep K step of both operand tiles is
-//    copied global -> LDS by buffer loads that write LDS directly (no VGPR
-//    staging), double-buffered; each wave then runs 16x16x128 E4M3 MFMAs on
-//    a (BM/2) x (BN/2) sub-tile with fp32 accumulators. The epilogue applies
+//  * gemm_tiled: many tokens (prompt reading). A workgroup of WGM x WGN
+//    waves owns a BM x BN output tile (256 x 192 with 2 x 4 waves: two waves
+//    per SIMD, so one wave's LDS reads overlap the other's MFMAs). Each
+//    128-deep K step of both operand tiles is copied global -> LDS by buffer
+//    loads that write LDS directly (no VGPR staging), double-buffered; each
+//    wave runs 16x16x128 E4M3 MFMAs on its (BM/WGM) x (BN/WGN) sub-tile with
+//    fp32 accumulators. The epilogue applies
 //    both scales in fp32, rounds to BF16 and goes through LDS so that every
 //    global store is a full 16-byte row segment. Workgroup ids are renumbered
 //    so that each of the 8 XCDs walks a compact block of tiles (its own L2).
@@ -31,27 +33,29 @@
 namespace w8a8 {
 namespace {
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 struct Tiled {
-  static constexpr int kThreads = 256;
-  static constexpr int WM = BM / 2, WN = BN / 2;       // per-wave tile (2 x 2 waves)
+  static constexpr int kThreads = 64 * WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wave tile
   static constexpr int SM = WM / 16, SN = WN / 16;     // 16x16 MFMA tiles per wave
   static constexpr int kRows = BM + BN;                // rows of one K-slice stage
   static constexpr int kStage = kRows * 128;           // bytes per stage
-  static constexpr int kLoads = kRows * 8 / kThreads;  // 16-byte loads per thread per stage
+  static constexpr int kRowsPerPass = kThreads / 8;    // rows one load instruction covers
+  static constexpr int kLoadsW = BN / kRowsPerPass;    // W loads per thread per stage
+  static constexpr int kLoads = kRows / kRowsPerPass;  // all loads per thread per stage
   static constexpr int kEpiStride = BN * 2 + 16;       // bytes per staged output row
   static constexpr int kEpi = BM * kEpiStride;
   static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
-  static_assert((kRows * 8) % kThreads == 0, "stage must split evenly over the threads");
+  static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
 };
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                 const uint8_t* __restrict__ W, const float* __restrict__ sw,
                 uint16_t* __restrict__ Y, int M, int N, int K, int tiles_m, int tiles_n) {
-  using C = Tiled<BM, BN>;
+  using C = Tiled<BM, BN, WGM, WGN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps rsrc / LDS bases scalar
@@ -61,28 +65,28 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
   const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
   const auto rA = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
 
-  // Loader: slot s = tid + 256 i is a 16-byte LDS slot; rows 0..BN-1 of a
-  // stage hold W, rows BN.. hold A. Lanes of a wave fill consecutive slots
-  // (8 rows of 128 bytes) and pick the global chunk that belongs in their
-  // slot. Slot s holds row (tid >> 3) + 32 i, and its logical chunk
-  // (tid & 7) ^ ((row >> 1) & 7) does not depend on i.
-  const int lchunk = ((tid & 7) ^ ((tid >> 4) & 7)) << 4;
+  // Loader: slot s = tid + kThreads * i is a 16-byte LDS slot; rows 0..BN-1
+  // of a stage hold W, rows BN.. hold A. Lanes of a wave fill consecutive
+  // slots (8 rows of 128 bytes) and pick the global chunk that belongs in
+  // their slot. Slot s holds row (tid >> 3) + kRowsPerPass * i, and its
+  // logical chunk (tid & 7) ^ (row & 7) does not depend on i.
+  const int lchunk = ((tid & 7) ^ ((tid >> 3) & 7)) << 4;
   const uint32_t lbase = (uint32_t)(tid >> 3) * (uint32_t)K + (uint32_t)lchunk;
-  constexpr int kLoadsW = BN / 32;
   auto issue = [&](int stage, int k0) {
     uint8_t* base = smem + stage * C::kStage;
     const bool kin = k0 + lchunk < K;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int s0 = wave * 64 + C::kThreads * i;  // first slot of this wave's 64
-      const int ii = i < kLoadsW ? i : i - kLoadsW;
-      const uint32_t off = kin ? lbase + (uint32_t)(32 * ii) * (uint32_t)K + (uint32_t)k0 : kOutOfRange;
-      if (i < kLoadsW) buffer_load16_lds(rW, base + s0 * 16, off);
-      else             buffer_load16_lds(rA, base + s0 * 16, off);
+      const int ii = i < C::kLoadsW ? i : i - C::kLoadsW;
+      const uint32_t off =
+          kin ? lbase + (uint32_t)(C::kRowsPerPass * ii) * (uint32_t)K + (uint32_t)k0 : kOutOfRange;
+      if (i < C::kLoadsW) buffer_load16_lds(rW, base + s0 * 16, off);
+      else                buffer_load16_lds(rA, base + s0 * 16, off);
     }
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int r16 = lane & 15, g = lane >> 4;
   v4f acc[C::SN][C::SM];
 #pragma unroll
@@ -222,12 +226,12 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 hipError_t run_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tiled<BM, BN>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, a, sa, w, sw, y,
-                     (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_tiled<BM, BN, WGM, WGN>), dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0, stream, a,
+                     sa, w, sw, y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -246,7 +250,7 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
                        y, (int)M, (int)N, (int)K);
     return hipGetLastError();
   }
-  return run_tiled<256, 192>(a, sa, w, sw, y, M, N, K, stream);
+  return run_tiled<256, 192, 2, 4>(a, sa, w, sw, y, M, N, K, stream);
 }
 
 }  // namespace w8a8

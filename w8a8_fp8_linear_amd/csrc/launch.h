@@ -18,22 +18,31 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
 
 // Routed-expert pipeline (moe.hip). offsets/perm are device arrays made by
 // launch_route; the grouped kernels derive their tiles from them on device.
-size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+// order 0: groups are experts (E groups); order 1: groups are (top-k
+// position j, expert) pairs, key j * E + e (topk * E groups).
+int64_t route_groups(int64_t topk, int64_t E, int order);
+size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t G);
 size_t grouped_gate_up_workspace_bytes(int64_t T, int64_t topk, int64_t E);
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 
-hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, void* scratch, hipStream_t stream);
+size_t gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk);
+
+// slot_row (may be NULL): slot -> its sorted row, -1 for a dropped id.
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int order, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* slot_row, void* scratch, hipStream_t stream);
 
 hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const uint8_t* w13, const float* s13,
                                        uint16_t* gu, int64_t T, int64_t H, int64_t I, int64_t E,
-                                       int64_t topk, hipStream_t stream);
+                                       int64_t topk, int order, hipStream_t stream);
 
+// dst_row (may be NULL): slot -> output row of h_q / h_scale; NULL keeps
+// the sorted order of perm. ws: gate_up_swiglu_quant_workspace_bytes bytes.
 hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
-                                       const int32_t* offsets, const uint8_t* w13, const float* s13,
-                                       uint8_t* qh, float* sh, int64_t T, int64_t H, int64_t I,
-                                       int64_t E, int64_t topk, hipStream_t stream);
+                                       const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
+                                       const float* s13, uint8_t* qh, float* sh, int64_t T, int64_t H,
+                                       int64_t I, int64_t E, int64_t topk, int order, void* ws,
+                                       hipStream_t stream);
 
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
                                const int32_t* offsets, const float* tw, const uint8_t* w2,

@@ -34,9 +34,16 @@
 //  * grouped_tiled<.., DOWN>: A = the requantised rows (already sorted and
 //    contiguous), B = W2 of the tile's expert; the epilogue multiplies by
 //    the slot scale, the channel scale and the router weight, stages the
-//    tile in LDS and adds it into a float32 [T, H] accumulator with atomics
-//    whose 64 lanes cover 64 consecutive outputs of one row.
+//    tile in LDS and adds it into a float32 [T, H] accumulator. The slots
+//    are sorted by (top-k position j, expert) and the down projection runs
+//    as one launch per j: inside a launch every token occurs at most once,
+//    so the accumulation is a plain read-add-write (no atomics; float32
+//    atomics measured ~3x slower than the whole alternative), and the k
+//    terms of a token are always added in the order j = 0, 1, ..., so the
+//    result is deterministic.
 //  * finalize: float32 accumulator -> BF16 (round to nearest even).
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -63,28 +70,36 @@ __device__ inline uint64_t match_peers(int key, int nbits) {
   return peers;
 }
 
-__global__ __launch_bounds__(256) void route_count(const int32_t* __restrict__ ids, int64_t n, int E,
-                                                   int32_t* __restrict__ chunk_counts) {
+// Group key of slot s with expert id e: e itself (expert-major order), or
+// (s % kdiv) * Eids + e (slot-position-major order, kdiv = top-k); -1 if the
+// id is outside [0, Eids).
+__device__ inline int group_key(int64_t s, int e, int Eids, int kdiv) {
+  if (e < 0 || e >= Eids) return -1;
+  return kdiv ? (int)(s % kdiv) * Eids + e : e;
+}
+
+__global__ __launch_bounds__(256) void route_count(const int32_t* __restrict__ ids, int64_t n, int Eids, int kdiv,
+                                                   int G, int32_t* __restrict__ chunk_counts) {
   extern __shared__ int hist[];
-  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  for (int e = threadIdx.x; e < G; e += 256) hist[e] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
   for (int i = threadIdx.x; i < kRouteChunk; i += 256) {
     const int64_t s = base + i;
     if (s < n) {
-      const int e = ids[s];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+      const int key = group_key(s, ids[s], Eids, kdiv);
+      if (key >= 0) atomicAdd(&hist[key], 1);
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+  for (int e = threadIdx.x; e < G; e += 256) chunk_counts[(int64_t)blockIdx.x * G + e] = hist[e];
 }
 
 // LDS: before[E] | base[4][E] | whist[4][E]
-__global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__ ids, int64_t n, int E, int nchunks,
-                                                     const int32_t* __restrict__ chunk_counts,
+__global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__ ids, int64_t n, int Eids, int kdiv,
+                                                     int E, int nchunks, const int32_t* __restrict__ chunk_counts,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm) {
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ slot_row) {
   extern __shared__ int sm[];
   int* before = sm;              // slots of expert e in earlier chunks, plus the expert's offset
   int* base = sm + E;            // per wave running position
@@ -92,19 +107,25 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
   for (int e = tid; e < 4 * E; e += 256) whist[e] = 0;
-  // totals and the exclusive scan over experts: wave 0 walks experts 64 at a time
+  // group totals and the counts of earlier chunks: every thread takes groups
+  // tid, tid + 256, ...; the exclusive scan over groups is then done by wave 0
+  for (int e = tid; e < E; e += 256) {
+    int tot = 0, bef = 0;
+#pragma unroll 8
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int v = chunk_counts[(int64_t)cc * E + e];
+      tot += v;
+      bef += cc < c ? v : 0;
+    }
+    base[e] = tot;      // base[] is free until the scatter; use it for totals
+    before[e] = bef;
+  }
+  __syncthreads();
   if (wave == 0) {
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
-      int tot = 0, bef = 0;
-      if (e < E) {
-        for (int cc = 0; cc < nchunks; ++cc) {
-          const int v = chunk_counts[(int64_t)cc * E + e];
-          tot += v;
-          if (cc < c) bef += v;
-        }
-      }
+      const int tot = e < E ? base[e] : 0;
       int incl = tot;
       for (int d = 1; d < 64; d <<= 1) {
         const int v = __shfl_up(incl, d, 64);
@@ -112,7 +133,7 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
       }
       const int off = carry + incl - tot;
       if (e < E) {
-        before[e] = off + bef;
+        before[e] += off;
         if (c == 0) {
           counts[e] = tot;
           offsets[e] = off;
@@ -134,8 +155,8 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
     const int64_t s = sub0 + i + lane;
     int key = E + 1;
     if (s < n) {
-      const int e = ids[s];
-      key = (e >= 0 && e < E) ? e : E;
+      const int k2 = group_key(s, ids[s], Eids, kdiv);
+      key = k2 >= 0 ? k2 : E;
     }
     const uint64_t peers = match_peers(key, nbits);
     const bool leader = lane == 63 - __clzll(peers);
@@ -156,13 +177,16 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
     const int64_t s = sub0 + i + lane;
     int key = E + 1;
     if (s < n) {
-      const int e = ids[s];
-      key = (e >= 0 && e < E) ? e : E;
+      const int k2 = group_key(s, ids[s], Eids, kdiv);
+      key = k2 >= 0 ? k2 : E;
     }
     const uint64_t peers = match_peers(key, nbits);
     if (key < E) {
       const int pos = base[wave * E + key] + __popcll(peers & lt);
       perm[pos] = (int32_t)s;
+      if (slot_row) slot_row[s] = pos;
+    } else if (slot_row && key == E) {
+      slot_row[s] = -1;  // dropped id
     }
     __builtin_amdgcn_wave_barrier();
     const bool leader = lane == 63 - __clzll(peers);
@@ -172,8 +196,10 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
 }
 
 // Which expert and which rows the m-tile `mt` covers, from the device-side
-// offsets (each wave computes it; the answer is uniform).
-__device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int BM, int mt, int& e_out,
+// offsets (each wave computes it; the answer is uniform). The rows are
+// clamped to [0, cap), the capacity of the sorted arrays, so inconsistent
+// offsets can never address outside them.
+__device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int BM, int mt, int cap, int& e_out,
                                  int& row0, int& rows) {
   const int lane = threadIdx.x & 63;
   int acc = 0;
@@ -200,108 +226,161 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
       e_out = __builtin_amdgcn_readfirstlane(e0 + src);
       row0 = __builtin_amdgcn_readfirstlane(st + local * BM);
       rows = __builtin_amdgcn_readfirstlane(min(BM, ct - local * BM));
-      return true;
+      if (row0 < 0 || row0 >= cap) return false;
+      rows = min(rows, cap - row0);
+      return rows > 0;
     }
     acc += __shfl(incl, 63, 64);
   }
   return false;
 }
 
-enum { kGateUp = 0, kDown = 1 };
+enum { kGateUp = 0, kDown = 1, kGateUpH = 2 };
 
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int WGM, int WGN, int MODE>
 struct Grouped {
-  static constexpr int kThreads = 256;
-  static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int SM = WM / 16, SN = WN / 16;
+  static constexpr int kThreads = 64 * WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wave tile
+  static constexpr int SM = WM / 16, SN = WN / 16;     // 16x16 MFMA tiles per wave
   static constexpr int kRows = BM + BN;
   static constexpr int kStage = kRows * 128;
-  static constexpr int kLoads = kRows * 8 / kThreads;
-  static constexpr int kOutElt = MODE == kGateUp ? 2 : 4;       // bf16 or fp32 staging
-  static constexpr int kEpiStride = BN * kOutElt + 16;
-  static constexpr int kEpi = BM * kEpiStride;
+  static constexpr int kRowsPerPass = kThreads / 8;    // rows one load instruction covers
+  static constexpr int kLoadsB = BN / kRowsPerPass, kLoadsA = BM / kRowsPerPass;
+  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP only)
+  static constexpr int kEpi = MODE == kGateUp ? BM * kEpiStride : 0;
   static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
-  static_assert((kRows * 8) % kThreads == 0, "stage must split evenly");
+  static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
+  static_assert(kRowsPerPass % 8 == 0, "the loader's chunk swizzle needs 8-row passes");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(MODE != kGateUpH || (SN % 2 == 0 && BN % 32 == 0), "gate/up block pairs must stay in one wave");
 };
 
-// Grouped GEMM over expert-sorted slots. M = sorted slots, N = output
-// columns of one expert's weight [N, K], K = reduction.
-//  GATE_UP: A row r = xq[perm[r] / topk] (gathered), out = gu bf16 [nslots, N]
-//           with scales xs[token] * sB[e, n].
-//  DOWN:    A row r = qh[r] (sorted, contiguous), out adds
-//           w[slot] * sh[r] * sB[e, n] * acc into acc32[token, n].
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sA, int64_t a_rows,
-                   const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets, int E, int topk,
-                   const uint8_t* __restrict__ B, const float* __restrict__ sB, const float* __restrict__ tw,
-                   uint16_t* __restrict__ out_bf16, float* __restrict__ out_acc, int N, int K, int tiles_n,
-                   int tiles_m_max) {
-  using C = Grouped<BM, BN, MODE>;
+struct GroupedArgs {
+  const uint8_t* A;         // GATE_UP*: x codes [a_rows, K]; DOWN: sorted h codes [a_rows, K]
+  const float* sA;          // GATE_UP*: token scales; DOWN: sorted row scales
+  int64_t a_rows;           // rows of A (tokens, or sorted rows)
+  const int32_t* perm;      // sorted row -> slot
+  const int32_t* offsets;   // [G + 1] group starts (device)
+  int G, Eids, topk;        // groups, experts (group g uses expert g % Eids), top-k
+  const uint8_t* B;         // [E, N, K] weight codes
+  const float* sB;          // [E, N] weight row scales
+  const float* tw;          // DOWN: router weights [slots]
+  uint16_t* out_bf16;       // GATE_UP: [rows, N]
+  float* out_f32;           // GATE_UP_H: h [rows, N / 2]; DOWN: accumulator [T, N]
+  uint32_t* row_amax;       // GATE_UP_H: max |h| bits per output row (cleared by the caller)
+  const int32_t* dst_row;   // GATE_UP_H: slot -> output row (NULL: the sorted row itself)
+  int N, K, tiles_n, tiles_m_max;
+};
+
+// Grouped GEMM over sorted slots: M = sorted rows, N = output columns of the
+// group's expert weight [N, K], K = reduction. Same pipeline as the dense
+// tiled kernel (WGM x WGN waves, 128-deep K steps staged global -> LDS by
+// direct buffer loads, double-buffered, 16x16x128 E4M3 MFMAs).
+//  GATE_UP:   A row = x[perm[r] / topk] (gathered); out = BF16 [r, N] with the
+//             scales x_scale[token] * sB[e, n].
+//  GATE_UP_H: as GATE_UP, but the stage's weight rows alternate a block of 16
+//             gate rows and the block of the 16 matching up rows (n-tile nt
+//             covers h columns [nt * BN/2, (nt + 1) * BN/2)), so the g and u
+//             of one h element land in the same lane and register. The
+//             epilogue forms h = silu(g) * u in float32, stores it to row
+//             dst_row[slot] (or r) of out_f32 [*, N/2], and posts the row's
+//             partial max |h| with an integer atomicMax on the float bits
+//             (order-independent, so the row maximum is exact).
+//  DOWN:      A row = h codes of sorted row r (contiguous); the epilogue adds
+//             w[slot] * sA[r] * sB[e, n] * acc to out_f32[token, n] straight
+//             from registers, a lane owning 4 consecutive columns of a row.
+//             The caller guarantees that a token occurs at most once per launch.
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
+void grouped_tiled(const GroupedArgs p) {
+  using C = Grouped<BM, BN, WGM, WGN, MODE>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   __shared__ int row_tok[BM];     // token of each tile row (-1 = empty row)
-  __shared__ float row_scale[BM]; // activation scale (times router weight for DOWN)
+  __shared__ float row_scale[BM]; // A scale (times the router weight for DOWN)
+  __shared__ int row_dst[BM];     // GATE_UP_H: output row (-1 = none)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // tile id -> (m-tile, n-tile); consecutive ids share the m-tile (A rows)
-  const int total = tiles_m_max * tiles_n;
+  const int N = p.N, K = p.K;
+  // tile id -> (m-tile, n-tile): each XCD walks a contiguous range, so the
+  // n-tiles of one m-tile (same A rows) and neighbouring m-tiles of one
+  // expert (same weights) share an L2
+  const int total = p.tiles_m_max * p.tiles_n;
   const int per = total >> 3;
   int t = blockIdx.x;
   if ((int)blockIdx.x < (per << 3)) t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int mt = t / tiles_n, nt = t - mt * tiles_n;
-  int e, row0, rows;
-  if (!find_tile(offsets, E, BM, mt, e, row0, rows)) return;
+  const int mt = t / p.tiles_n, nt = t - mt * p.tiles_n;
+  const int cap = (int)(MODE != kDown ? p.a_rows * p.topk : p.a_rows);  // sorted-row capacity
+  int grp, row0, rows;
+  if (!find_tile(p.offsets, p.G, BM, mt, cap, grp, row0, rows)) return;
+  const int e = grp % p.Eids;
   const int n0 = nt * BN;
 
   for (int i = tid; i < BM; i += C::kThreads) {
-    int tok = -1;
+    int tok = -1, dst = -1;
     float sc = 0.f;
     if (i < rows) {
-      const int slot = perm[row0 + i];
-      tok = slot / topk;
-      sc = MODE == kGateUp ? sA[tok] : sA[row0 + i] * tw[slot];
+      const int slot = p.perm[row0 + i];
+      if (slot >= 0 && slot < cap) {
+        tok = slot / p.topk;
+        sc = MODE != kDown ? p.sA[tok] : p.sA[row0 + i] * p.tw[slot];
+        if (MODE == kGateUpH) {
+          dst = p.dst_row ? p.dst_row[slot] : row0 + i;
+          if (dst >= cap) dst = -1;
+        }
+      }
     }
     row_tok[i] = tok;
     row_scale[i] = sc;
+    row_dst[i] = dst;
   }
   __syncthreads();
 
-  const auto rB = make_rsrc(B + ((int64_t)e * N + n0) * K, (int64_t)(N - n0) * K);
-  const auto rA = MODE == kGateUp ? make_rsrc(A, a_rows * K) : make_rsrc(A + (int64_t)row0 * K, (int64_t)rows * K);
-  // Loader (as in the dense kernel): thread tid fills rows (tid >> 3) + 32 i,
-  // always with logical chunk (tid & 7) ^ ((tid >> 4) & 7). B rows first.
-  const int lchunk = ((tid & 7) ^ ((tid >> 4) & 7)) << 4;
-  constexpr int kLoadsB = BN / 32, kLoadsA = BM / 32;
-  const uint32_t bbase = (uint32_t)(tid >> 3) * (uint32_t)K + (uint32_t)lchunk;
-  uint32_t aoff[kLoadsA];
+  const auto rB = MODE == kGateUpH ? make_rsrc(p.B + (int64_t)e * N * K, (int64_t)N * K)
+                                    : make_rsrc(p.B + ((int64_t)e * N + n0) * K, (int64_t)(N - n0) * K);
+  const auto rA = MODE != kDown ? make_rsrc(p.A, p.a_rows * K)
+                                : make_rsrc(p.A + (int64_t)row0 * K, (int64_t)rows * K);
+  // Loader (as in the dense kernel): LDS slot tid + kThreads * i holds stage
+  // row (tid >> 3) + kRowsPerPass * i, logical chunk (tid & 7) ^ (row & 7).
+  // Stage rows 0..BN-1 hold B, rows BN.. hold A.
+  const int lchunk = ((tid & 7) ^ ((tid >> 3) & 7)) << 4;
+  const int lrow = tid >> 3;
+  uint32_t boff[C::kLoadsB], aoff[C::kLoadsA];
 #pragma unroll
-  for (int j = 0; j < kLoadsA; ++j) {
-    const int lr = (tid >> 3) + 32 * j;
-    if (MODE == kGateUp) {
+  for (int i = 0; i < C::kLoadsB; ++i) {
+    const int r = lrow + C::kRowsPerPass * i;
+    int wr = r;
+    if (MODE == kGateUpH) {  // 16-row block b: even = gate rows, odd = the matching up rows
+      const int b = r >> 4;
+      wr = (b & 1 ? N / 2 : 0) + (n0 >> 1) + (b >> 1) * 16 + (r & 15);
+    }
+    boff[i] = (uint32_t)wr * (uint32_t)K + (uint32_t)lchunk;
+  }
+#pragma unroll
+  for (int j = 0; j < C::kLoadsA; ++j) {
+    const int lr = lrow + C::kRowsPerPass * j;
+    if (MODE != kDown) {
       const int tok = row_tok[lr];
       aoff[j] = tok < 0 ? kOutOfRange : (uint32_t)tok * (uint32_t)K + (uint32_t)lchunk;
     } else {
-      aoff[j] = (uint32_t)lr * (uint32_t)K + (uint32_t)lchunk;
+      aoff[j] = lr < rows ? (uint32_t)lr * (uint32_t)K + (uint32_t)lchunk : kOutOfRange;
     }
   }
   auto issue = [&](int stage, int k0) {
     uint8_t* base = smem + stage * C::kStage;
     const bool kin = k0 + lchunk < K;
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int s0 = wave * 64 + C::kThreads * i;
-      if (i < kLoadsB) {
-        const uint32_t off = kin ? bbase + (uint32_t)(32 * i) * (uint32_t)K + (uint32_t)k0 : kOutOfRange;
-        buffer_load16_lds(rB, base + s0 * 16, off);
+    for (int i = 0; i < C::kLoadsB + C::kLoadsA; ++i) {
+      const int s0 = wave * 64 + C::kThreads * i;  // first LDS slot of this wave's 64
+      if (i < C::kLoadsB) {
+        buffer_load16_lds(rB, base + s0 * 16, kin ? boff[i] + (uint32_t)k0 : kOutOfRange);
       } else {
-        const uint32_t a = aoff[i - kLoadsB];
-        const uint32_t off = (kin && a != kOutOfRange) ? a + (uint32_t)k0 : kOutOfRange;
-        buffer_load16_lds(rA, base + s0 * 16, off);
+        const uint32_t a = aoff[i - C::kLoadsB];
+        buffer_load16_lds(rA, base + s0 * 16, (kin && a != kOutOfRange) ? a + (uint32_t)k0 : kOutOfRange);
       }
     }
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int r16 = lane & 15, g = lane >> 4;
   v4f acc[C::SN][C::SM];
 #pragma unroll
@@ -333,215 +412,143 @@ void grouped_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sA, 
       for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf, xf[j], acc[i][j]);
     }
   }
+
+  // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
+  // wn * WN + 16 i + 4 (lane / 16) + r.
+  if (MODE == kDown) {
+    int toks[C::SM];
+    float rs[C::SM];
+#pragma unroll
+    for (int j = 0; j < C::SM; ++j) {
+      const int ml = wm * C::WM + j * 16 + r16;
+      toks[j] = row_tok[ml];
+      rs[j] = row_scale[ml];
+    }
+#pragma unroll
+    for (int i = 0; i < C::SN; ++i) {
+      const int n = n0 + wn * C::WN + i * 16 + 4 * g;
+      if (n >= N) continue;
+      const float4 sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n);
+      float4 cur[C::SM];
+#pragma unroll
+      for (int j = 0; j < C::SM; ++j)
+        cur[j] = toks[j] >= 0 ? *reinterpret_cast<const float4*>(p.out_f32 + (int64_t)toks[j] * N + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < C::SM; ++j) {
+        if (toks[j] < 0) continue;
+        const v4f a = acc[i][j];
+        const float s = rs[j];
+        float4 c = cur[j];
+        c.x += a[0] * s * sW.x;
+        c.y += a[1] * s * sW.y;
+        c.z += a[2] * s * sW.z;
+        c.w += a[3] * s * sW.w;
+        *reinterpret_cast<float4*>(p.out_f32 + (int64_t)toks[j] * N + n) = c;
+      }
+    }
+    return;
+  }
+  if (MODE == kGateUpH) {
+    const int Ih = N / 2;
+    int dsts[C::SM];
+    float rs[C::SM], amax[C::SM];
+#pragma unroll
+    for (int j = 0; j < C::SM; ++j) {
+      const int ml = wm * C::WM + j * 16 + r16;
+      dsts[j] = row_dst[ml];
+      rs[j] = row_scale[ml];
+      amax[j] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < C::SN; i += 2) {  // i: gate block, i + 1: its up block
+      const int sr = wn * C::WN + i * 16;
+      const int hc = (n0 >> 1) + ((sr >> 5) << 4) + 4 * g;  // h column of this lane's first value
+      const float4 gs4 = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + hc);
+      const float4 us4 = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + Ih + hc);
+      const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w}, us[4] = {us4.x, us4.y, us4.z, us4.w};
+#pragma unroll
+      for (int j = 0; j < C::SM; ++j) {
+        const v4f ga = acc[i][j], ua = acc[i + 1][j];
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gv = ga[r] * rs[j] * gs[r];
+          const float uv = ua[r] * rs[j] * us[r];
+          h[r] = gv / (1.0f + __expf(-gv)) * uv;
+          amax[j] = fmaxf(amax[j], fabsf(h[r]));
+        }
+        if (dsts[j] >= 0)
+          *reinterpret_cast<float4*>(p.out_f32 + (int64_t)dsts[j] * Ih + hc) = make_float4(h[0], h[1], h[2], h[3]);
+      }
+    }
+    // lane groups g = 0..3 hold the same rows: reduce over them, one atomic per row
+#pragma unroll
+    for (int j = 0; j < C::SM; ++j) {
+      float m = amax[j];
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (g == 0 && dsts[j] >= 0) atomicMax(p.row_amax + dsts[j], __float_as_uint(m));
+    }
+    return;
+  }
+  // GATE_UP: scale, round to BF16, stage in LDS, store full row segments
   __syncthreads();
-  // stage the scaled tile in LDS: acc[i][j][r] is row (m-tile j, lane % 16), columns
-  // (n-tile i, 4 * (lane / 16) + r)
 #pragma unroll
   for (int i = 0; i < C::SN; ++i) {
     const int nl = wn * C::WN + i * 16 + 4 * g;
     float4 sW = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (n0 + nl < N) sW = *reinterpret_cast<const float4*>(sB + (int64_t)e * N + n0 + nl);
+    if (n0 + nl < N) sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl);
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
       const float s = row_scale[ml];
       const v4f a = acc[i][j];
-      if (MODE == kGateUp) {
-        const uint32_t b0 = f32_to_bf16_rne(a[0] * s * sW.x), b1 = f32_to_bf16_rne(a[1] * s * sW.y);
-        const uint32_t b2 = f32_to_bf16_rne(a[2] * s * sW.z), b3 = f32_to_bf16_rne(a[3] * s * sW.w);
-        *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-      } else {
-        *reinterpret_cast<float4*>(smem + ml * C::kEpiStride + nl * 4) =
-            make_float4(a[0] * s * sW.x, a[1] * s * sW.y, a[2] * s * sW.z, a[3] * s * sW.w);
-      }
+      const uint32_t b0 = f32_to_bf16_rne(a[0] * s * sW.x), b1 = f32_to_bf16_rne(a[1] * s * sW.y);
+      const uint32_t b2 = f32_to_bf16_rne(a[2] * s * sW.z), b3 = f32_to_bf16_rne(a[3] * s * sW.w);
+      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
     }
   }
   __syncthreads();
-  if (MODE == kGateUp) {
-    constexpr int kRowChunks = BN / 8;
-    for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
-      const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
-      if (row < rows && n0 + col < N)
-        *reinterpret_cast<uint4*>(out_bf16 + (int64_t)(row0 + row) * N + n0 + col) =
-            *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
-    }
-  } else {
-    // one wave per row at a time, 64 consecutive columns per atomic instruction
-    for (int row = wave; row < rows; row += 4) {
-      const int tok = row_tok[row];
-      float* dst = out_acc + (int64_t)tok * N + n0;
-      const float* src = reinterpret_cast<const float*>(smem + row * C::kEpiStride);
-      for (int col = lane; col < BN && n0 + col < N; col += 64) atomicAdd(dst + col, src[col]);
-    }
+  constexpr int kRowChunks = BN / 8;
+  for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
+    const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
+    if (row < rows && n0 + col < N)
+      *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)(row0 + row) * N + n0 + col) =
+          *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
   }
 }
 
-// ---- fused gate/up + SwiGLU + per-slot requantisation ----------------------
-// Workgroup: 64 sorted slots x all 2I columns; wave w owns gate columns
-// [64w, 64w + 64) and up columns [I + 64w, I + 64w + 64). K steps of 64.
-constexpr int kFBM = 64;
-constexpr int kFStageA = kFBM * 64;      // 64 rows x 64 bytes
+// Requantisation of float32 h rows, elementwise once the row maxima are
+// known: s_r = fl32(amax_r / 448) (1 for an all-zero row), q = E4M3(fl32(h / s_r))
+// (IEEE division, round to nearest even, saturating). One thread per 16
+// values of a row; rows from the valid count on are left alone.
+__global__ __launch_bounds__(256) void requant_rows(const float* __restrict__ h, const uint32_t* __restrict__ amax_bits,
+                                                    const int32_t* __restrict__ nvalid, int64_t cap, int I,
+                                                    uint8_t* __restrict__ qh, float* __restrict__ sh) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = I >> 4;
+  const int64_t row = i / per_row;
+  const int64_t nrows = min((int64_t)*nvalid, cap);
+  if (row >= nrows) return;
+  const int c0 = (int)(i - row * per_row) << 4;
+  const float amax = __uint_as_float(amax_bits[row]);
+  const float s = amax == 0.f ? 1.0f : amax / 448.0f;
+  const float4* src = reinterpret_cast<const float4*>(h + row * I + c0);
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = src[q];
+    w[q] = e4m3_rne_sat(v.x / s) | (e4m3_rne_sat(v.y / s) << 8) | (e4m3_rne_sat(v.z / s) << 16) |
+           (e4m3_rne_sat(v.w / s) << 24);
+  }
+  *reinterpret_cast<uint4*>(qh + row * I + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+  if (c0 == 0) sh[row] = s;
+}
 
-template <int WAVES>
-struct Fused {
-  static_assert(WAVES == 4 || WAVES == 8, "the A loader uses 256 threads; rows split over 4 or 8 waves");
-  static constexpr int I = 64 * WAVES;
-  static constexpr int kThreads = 64 * WAVES;
-  static constexpr int kHStride = I * 4 + 16;               // fp32 h row in LDS
-  static constexpr int kH = kFBM * kHStride;
-  static constexpr int kLds = (2 * kFStageA > kH) ? 2 * kFStageA : kH;
-};
-
-// byte offset of 16-byte chunk c (0..3) of row `row` in a 64-byte-row stage
-__device__ inline int stage64_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
-
-template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void gate_up_swiglu_quant(const uint8_t* __restrict__ xq, const float* __restrict__ xs, int64_t T,
-                          const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets, int E, int topk,
-                          const uint8_t* __restrict__ w13, const float* __restrict__ s13,
-                          uint8_t* __restrict__ qh, float* __restrict__ sh, int H) {
-  using F = Fused<WAVES>;
-  constexpr int I = F::I;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[F::kLds];
-  __shared__ int row_tok[kFBM];
-  __shared__ float row_xs[kFBM];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int e, row0, rows;
-  if (!find_tile(offsets, E, kFBM, blockIdx.x, e, row0, rows)) return;
-  for (int i = tid; i < kFBM; i += F::kThreads) {
-    int tok = -1;
-    float s = 0.f;
-    if (i < rows) {
-      tok = perm[row0 + i] / topk;
-      s = xs[tok];
-    }
-    row_tok[i] = tok;
-    row_xs[i] = s;
-  }
-  __syncthreads();
-  const auto rA = make_rsrc(xq, T * H);
-  const auto rB = make_rsrc(w13 + (int64_t)e * 2 * I * H, (int64_t)2 * I * H);
-  // A loader: threads 0..255 each move one 16-byte chunk per K step
-  uint32_t aoff = kOutOfRange;
-  int achunk = 0;
-  if (tid < 256) {
-    const int row = tid >> 2, c = (tid & 3) ^ ((row >> 2) & 3);
-    achunk = c << 4;
-    const int tok = row_tok[row];
-    if (tok >= 0) aoff = (uint32_t)tok * (uint32_t)H + (uint32_t)achunk;
-  }
-  auto issueA = [&](int stage, int k0) {
-    if (wave < 4) {
-      const uint32_t off = (aoff != kOutOfRange && k0 + achunk < H) ? aoff + (uint32_t)k0 : kOutOfRange;
-      buffer_load16_lds(rA, smem + stage * kFStageA + wave * 1024, off);
-    }
-  };
-  // B: lane holds row (lane % 32) of each of its 4 column tiles, 16-byte
-  // chunks hb and hb + 2 of the 64-byte K slice (hb = lane / 32)
-  const int r32 = lane & 31, hb = lane >> 5;
-  uint32_t brow[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int col = (ct < 2 ? 0 : I) + 64 * wave + 32 * (ct & 1) + r32;
-    brow[ct] = (uint32_t)col * (uint32_t)H;
-  }
-  auto loadB = [&](v8i (&bf)[4], int k0) {
-    const int c0 = k0 + 16 * hb, c1 = c0 + 32;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const v4i lo = buffer_load16(rB, c0 < H ? brow[ct] + c0 : kOutOfRange);
-      const v4i hi = buffer_load16(rB, c1 < H ? brow[ct] + c1 : kOutOfRange);
-      bf[ct] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-  };
-  v16f acc[2][4];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[rt][ct][q] = 0.f;
-  const int nk = (H + 63) >> 6;
-  v8i bcur[4], bnext[4];
-  issueA(0, 0);
-  loadB(bcur, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmem_all();
-    __syncthreads();
-    if (kt + 1 < nk) {
-      issueA((kt + 1) & 1, (kt + 1) << 6);
-      loadB(bnext, (kt + 1) << 6);
-    }
-    const uint8_t* st = smem + (kt & 1) * kFStageA;
-    v8i af[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int row = rt * 32 + r32;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + stage64_off(row, hb));
-      const v4i hi = *reinterpret_cast<const v4i*>(st + stage64_off(row, hb + 2));
-      af[rt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) acc[rt][ct] = mfma_32x32x64_e4m3(bcur[ct], af[rt], acc[rt][ct]);
-    if (kt + 1 < nk) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) bcur[ct] = bnext[ct];
-    }
-  }
-  __syncthreads();
-  // Epilogue 1: acc[rt][ct][q] = column (ct tile, 8 * (q / 4) + 4 * (lane / 32) + q % 4),
-  // slot row (rt * 32 + lane % 32). Gate tiles ct = 0, 1 pair with up tiles ct = 2, 3.
-  float* hbuf = reinterpret_cast<float*>(smem);
-  {
-    const int ml0 = r32;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int ml = rt * 32 + ml0;
-      const float s = row_xs[ml];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int cl = 8 * (q >> 2) + 4 * hb + (q & 3);       // 0..31 inside the tile
-          const int j = 64 * wave + 32 * half + cl;           // h column
-          const float gs = s13[(int64_t)e * 2 * I + j], us = s13[(int64_t)e * 2 * I + I + j];
-          const float gv = acc[rt][half][q] * s * gs;
-          const float uv = acc[rt][2 + half][q] * s * us;
-          const float h = gv / (1.0f + __expf(-gv)) * uv;
-          hbuf[ml * (F::kHStride / 4) + j] = h;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // Epilogue 2: one wave per row: amax, scale, E4M3 codes (I / 64 values per lane)
-  constexpr int PER = I / 64;
-  for (int row = wave; row < rows; row += WAVES) {
-    const float* hr = hbuf + row * (F::kHStride / 4);
-    float v[PER];
-    float amax = 0.f;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      v[p] = hr[lane * PER + p];
-      amax = fmaxf(amax, fabsf(v[p]));
-    }
-    amax = wave_max_f32(amax);
-    const float s = amax == 0.f ? 1.0f : amax / 448.0f;
-    uint8_t* dst = qh + (int64_t)(row0 + row) * I + lane * PER;
-    uint32_t words[PER / 4];
-#pragma unroll
-    for (int p = 0; p < PER / 4; ++p) {
-      words[p] = e4m3_rne_sat(v[4 * p] / s) | (e4m3_rne_sat(v[4 * p + 1] / s) << 8) |
-                 (e4m3_rne_sat(v[4 * p + 2] / s) << 16) | (e4m3_rne_sat(v[4 * p + 3] / s) << 24);
-    }
-#pragma unroll
-    for (int p = 0; p < PER / 4; ++p) reinterpret_cast<uint32_t*>(dst)[p] = words[p];
-    if (lane == 0) sh[row0 + row] = s;
-  }
+__global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_f32(float* __restrict__ p, int64_t n4) {
@@ -567,93 +574,161 @@ int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
 int route_chunks(int64_t n) { return (int)((n + kRouteChunk - 1) / kRouteChunk); }
 
-constexpr int kGUBM = 128, kGUBN = 256;   // bf16 gate/up tiles
-constexpr int kDNBM = 128, kDNBN = 256;   // down + combine tiles
+// Tile shapes. The gate/up runs on expert-major groups (about T*k/E rows
+// each): 256 x 256 tiles, 8 waves of 128 x 64. The down projection runs once
+// per top-k position on groups of about T/E rows: 128 x 128 tiles, 4 waves,
+// two workgroups per CU so that one's read-add-write epilogue overlaps the
+// other's MFMAs.
+constexpr int kGuBM = 256, kGuBN = 256, kGuWGM = 2, kGuWGN = 4, kGuOcc = 2;
+constexpr int kDnBM = 128, kDnBN = 128, kDnWGM = 2, kDnWGN = 2, kDnOcc = 2;
+
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
+hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
+  a.tiles_n = (a.N + BN - 1) / BN;
+  a.tiles_m_max = (int)((max_rows + BM - 1) / BM + a.G);  // every group adds at most one partial tile
+  const int64_t blocks = (int64_t)a.tiles_m_max * a.tiles_n;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_tiled<BM, BN, WGM, WGN, MODE, OCC>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+GroupedArgs gate_up_args(const uint8_t* xq, const float* xs, const int32_t* perm, const int32_t* offsets, int G,
+                         const uint8_t* w13, const float* s13, int64_t T, int64_t H, int64_t I, int64_t E,
+                         int64_t topk) {
+  GroupedArgs a{};
+  a.A = xq;
+  a.sA = xs;
+  a.a_rows = T;
+  a.perm = perm;
+  a.offsets = offsets;
+  a.G = G;
+  a.Eids = (int)E;
+  a.topk = (int)topk;
+  a.B = w13;
+  a.sB = s13;
+  a.N = (int)(2 * I);
+  a.K = (int)H;
+  return a;
+}
 
 }  // namespace
 
-size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
-  return (size_t)align256((int64_t)route_chunks(T * topk) * E * 4);
+size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t G) {
+  return (size_t)align256((int64_t)route_chunks(T * topk) * G * 4);
 }
 
-hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, void* scratch, hipStream_t stream) {
+int64_t route_groups(int64_t topk, int64_t E, int order) { return order ? topk * E : E; }
+
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int order, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* slot_row, void* scratch, hipStream_t stream) {
   const int64_t n = T * topk;
   const int nch = route_chunks(n);
   if (nch == 0) return hipSuccess;
+  const int G = (int)route_groups(topk, E, order);
+  const int kdiv = order ? (int)topk : 0;
   int32_t* chunk_counts = static_cast<int32_t*>(scratch);
-  hipLaunchKernelGGL(route_count, dim3(nch), dim3(256), (size_t)E * 4, stream, ids, n, (int)E, chunk_counts);
-  hipLaunchKernelGGL(route_scatter, dim3(nch), dim3(256), (size_t)E * 9 * 4, stream, ids, n, (int)E, nch,
-                     chunk_counts, counts, offsets, perm);
+  hipLaunchKernelGGL(route_count, dim3(nch), dim3(256), (size_t)G * 4, stream, ids, n, (int)E, kdiv, G,
+                     chunk_counts);
+  hipLaunchKernelGGL(route_scatter, dim3(nch), dim3(256), (size_t)G * 9 * 4, stream, ids, n, (int)E, kdiv, G, nch,
+                     chunk_counts, counts, offsets, perm, slot_row);
   return hipGetLastError();
 }
-
-static int64_t m_tiles_max(int64_t nslots, int64_t E, int BM) { return (nslots + BM - 1) / BM + E; }
 
 hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const uint8_t* w13, const float* s13, uint16_t* gu,
-                                       int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                                       int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
                                        hipStream_t stream) {
-  const int N = (int)(2 * I);
-  const int tiles_n = (N + kGUBN - 1) / kGUBN;
-  const int tiles_m = (int)m_tiles_max(T * topk, E, kGUBM);
-  hipLaunchKernelGGL((grouped_tiled<kGUBM, kGUBN, kGateUp>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, xq, xs,
-                     T, perm, offsets, (int)E, (int)topk, w13, s13, (const float*)nullptr, gu, (float*)nullptr, N,
-                     (int)H, tiles_n, tiles_m);
-  return hipGetLastError();
+  GroupedArgs a = gate_up_args(xq, xs, perm, offsets, (int)route_groups(topk, E, order), w13, s13, T, H, I, E, topk);
+  a.out_bf16 = gu;
+  return run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, kGateUp, kGuOcc>(a, T * topk, stream);
 }
 
+size_t gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk) {
+  const int64_t n = T * topk;
+  return (size_t)(align256(n * 4) + align256(n * I * 4));
+}
+
+// Workspace: row maxima [T*k] (uint32 float bits) | h [T*k, I] float32.
 hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
-                                       const int32_t* offsets, const uint8_t* w13, const float* s13, uint8_t* qh,
-                                       float* sh, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
-                                       hipStream_t stream) {
-  const dim3 grid((unsigned)m_tiles_max(T * topk, E, kFBM));
-  switch (I) {
-#define W8A8_FUSED(WV)                                                                                   \
-  case 64 * WV:                                                                                          \
-    hipLaunchKernelGGL((gate_up_swiglu_quant<WV>), grid, dim3(64 * WV), 0, stream, xq, xs, T, perm,       \
-                       offsets, (int)E, (int)topk, w13, s13, qh, sh, (int)H);                             \
-    break;
-    W8A8_FUSED(4) W8A8_FUSED(8)
-#undef W8A8_FUSED
-    default:
-      return hipErrorInvalidValue;
-  }
+                                       const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
+                                       const float* s13, uint8_t* qh, float* sh, int64_t T, int64_t H, int64_t I,
+                                       int64_t E, int64_t topk, int order, void* ws, hipStream_t stream) {
+  const int64_t n = T * topk;
+  if (n == 0) return hipSuccess;
+  const int G = (int)route_groups(topk, E, order);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  float* h = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * 4));
+  hipLaunchKernelGGL(fill_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, amax, n);
+  GroupedArgs a = gate_up_args(xq, xs, perm, offsets, G, w13, s13, T, H, I, E, topk);
+  a.out_f32 = h;
+  a.row_amax = amax;
+  a.dst_row = dst_row;
+  hipError_t err = run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, kGateUpH, kGuOcc>(a, n, stream);
+  if (err != hipSuccess) return err;
+  const int64_t threads = n * (I / 16);
+  hipLaunchKernelGGL(requant_rows, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, h, amax,
+                     offsets + G, n, (int)I, qh, sh);
   return hipGetLastError();
 }
 
+// Needs the slot-position-major order (order = 1): launch j covers groups
+// [j * E, (j + 1) * E), in which every token occurs at most once.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm, const int32_t* offsets,
                                const float* tw, const uint8_t* w2, const float* s2, uint16_t* out, float* acc,
                                int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
   const int64_t n4 = T * H / 4;
   hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, acc, n4);
-  const int N = (int)H;
-  const int tiles_n = (N + kDNBN - 1) / kDNBN;
-  const int tiles_m = (int)m_tiles_max(T * topk, E, kDNBM);
-  hipLaunchKernelGGL((grouped_tiled<kDNBM, kDNBN, kDown>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, qh, sh,
-                     T * topk, perm, offsets, (int)E, (int)topk, w2, s2, tw, (uint16_t*)nullptr, acc, N, (int)I,
-                     tiles_n, tiles_m);
+  GroupedArgs a{};
+  a.A = qh;
+  a.sA = sh;
+  a.a_rows = T * topk;
+  a.perm = perm;
+  a.G = (int)E;
+  a.Eids = (int)E;
+  a.topk = (int)topk;
+  a.B = w2;
+  a.sB = s2;
+  a.tw = tw;
+  a.out_f32 = acc;
+  a.N = (int)H;
+  a.K = (int)I;
+  for (int64_t j = 0; j < topk; ++j) {
+    a.offsets = offsets + j * E;
+    const hipError_t err = run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, kDown, kDnOcc>(a, T, stream);
+    if (err != hipSuccess) return err;
+  }
   const int64_t n8 = T * H / 8;
   hipLaunchKernelGGL(finalize_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, acc, out, n8);
   return hipGetLastError();
 }
 
-// Workspace of the full pass: counts | offsets | perm | route scratch | qh | sh | acc
+// Workspace of the full pass:
+//   counts0 | offsets0 | perm0          expert-major routing (gate/up tiles)
+//   counts1 | offsets1 | perm1 | row1   position-major routing (down launches)
+//   route scratch | qh | sh | amax | big
+// where big holds h [T*k, I] float32 during the gate/up and then the float32
+// [T, H] accumulator of the down projection.
 struct MoeLayout {
-  int64_t counts, offsets, perm, route, qh, sh, acc, total;
+  int64_t counts0, offsets0, perm0, counts1, offsets1, perm1, row1, route, qh, sh, amax, big, total;
 };
 
 static MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
   MoeLayout L;
   int64_t o = 0;
-  const int64_t n = T * topk;
-  L.counts = o; o += align256(E * 4);
-  L.offsets = o; o += align256((E + 1) * 4);
-  L.perm = o; o += align256(n * 4);
-  L.route = o; o += (int64_t)route_workspace_bytes(T, topk, E);
+  const int64_t n = T * topk, G1 = route_groups(topk, E, 1);
+  L.counts0 = o; o += align256(E * 4);
+  L.offsets0 = o; o += align256((E + 1) * 4);
+  L.perm0 = o; o += align256(n * 4);
+  L.counts1 = o; o += align256(G1 * 4);
+  L.offsets1 = o; o += align256((G1 + 1) * 4);
+  L.perm1 = o; o += align256(n * 4);
+  L.row1 = o; o += align256(n * 4);
+  L.route = o; o += (int64_t)route_workspace_bytes(T, topk, G1);
   L.qh = o; o += align256(n * I);
   L.sh = o; o += align256(n * 4);
-  L.acc = o; o += align256(T * H * 4);
+  L.amax = o; o += align256(n * 4);  // amax | big is the gate/up stage's workspace
+  L.big = o; o += std::max(align256(n * I * 4), align256(T * H * 4));
   L.total = o;
   return L;
 }
@@ -662,22 +737,28 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t t
   return (size_t)moe_layout(T, H, I, E, topk).total;
 }
 
+// One pass: the gate/up tiles follow the expert-major order (large groups,
+// each expert's weights streamed once per 256 rows) and write each h row at
+// its position-major row, which the down launches then read contiguously.
 hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, const float* tw, const uint8_t* w13,
                       const float* s13, const uint8_t* w2, const float* s2, uint16_t* out, int64_t T, int64_t H,
                       int64_t I, int64_t E, int64_t topk, void* ws, hipStream_t stream) {
   const MoeLayout L = moe_layout(T, H, I, E, topk);
   uint8_t* b = static_cast<uint8_t*>(ws);
-  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
-  int32_t* perm = reinterpret_cast<int32_t*>(b + L.perm);
+  auto i32 = [&](int64_t off) { return reinterpret_cast<int32_t*>(b + off); };
+  hipError_t err = launch_route(ids, T, topk, E, 0, i32(L.counts0), i32(L.offsets0), i32(L.perm0), nullptr,
+                                b + L.route, stream);
+  if (err != hipSuccess) return err;
+  err = launch_route(ids, T, topk, E, 1, i32(L.counts1), i32(L.offsets1), i32(L.perm1), i32(L.row1), b + L.route,
+                     stream);
+  if (err != hipSuccess) return err;
   uint8_t* qh = b + L.qh;
   float* sh = reinterpret_cast<float*>(b + L.sh);
-  float* acc = reinterpret_cast<float*>(b + L.acc);
-  hipError_t err = launch_route(ids, T, topk, E, counts, offsets, perm, b + L.route, stream);
+  err = launch_gate_up_swiglu_quant(xq, xs, i32(L.perm0), i32(L.offsets0), i32(L.row1), w13, s13, qh, sh, T, H, I, E,
+                                    topk, 0, b + L.amax, stream);
   if (err != hipSuccess) return err;
-  err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, w13, s13, qh, sh, T, H, I, E, topk, stream);
-  if (err != hipSuccess) return err;
-  return launch_down_combine(qh, sh, perm, offsets, tw, w2, s2, out, acc, T, H, I, E, topk, stream);
+  return launch_down_combine(qh, sh, i32(L.perm1), i32(L.offsets1), tw, w2, s2, out,
+                             reinterpret_cast<float*>(b + L.big), T, H, I, E, topk, stream);
 }
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids, const uint8_t* w13,
@@ -685,9 +766,9 @@ hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int3
                                   int64_t H, int64_t I, int64_t E, int64_t topk, void* ws, hipStream_t stream) {
   uint8_t* b = static_cast<uint8_t*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(b);
-  hipError_t err = launch_route(ids, T, topk, E, counts, offsets, perm, b + align256(E * 4), stream);
+  hipError_t err = launch_route(ids, T, topk, E, 0, counts, offsets, perm, nullptr, b + align256(E * 4), stream);
   if (err != hipSuccess) return err;
-  return launch_grouped_gate_up_bf16(xq, xs, perm, offsets, w13, s13, gu, T, H, I, E, topk, stream);
+  return launch_grouped_gate_up_bf16(xq, xs, perm, offsets, w13, s13, gu, T, H, I, E, topk, 0, stream);
 }
 
 size_t grouped_gate_up_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
