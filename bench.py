@@ -236,8 +236,7 @@ def bench_moe_two_pass(reps=5, warmup=2):
     stages = {}
     for name, fn in (
         ("quantize", lambda: w8.quantize_per_token(x, xq, xs)),
-        ("route_both_orders", lambda: (w8.moe_route(ids, E, order=0),
-                                       w8.moe_route(ids, E, order=1, with_slot_row=True))),
+        ("route", lambda: w8.moe_route(ids, E, order=0)),
     ):
         ev = _events(reps)
         for a, b in ev:
@@ -245,17 +244,16 @@ def bench_moe_two_pass(reps=5, warmup=2):
         torch.cuda.synchronize()
         stages[name] = 1e3 * _avg_ms(ev)
     _, off0, perm0 = w8.moe_route(ids, E, order=0)
-    _, off1, perm1, row1 = w8.moe_route(ids, E, order=1, with_slot_row=True)
     gu_ws = torch.empty(int(w8.lib().moe_gate_up_swiglu_quant_workspace_bytes(T, I, k)), dtype=torch.uint8,
                         device="cuda")
-    hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0, dst_row=row1, workspace=gu_ws)
+    hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0, workspace=gu_ws)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    acc = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
     for name, fn, fl in (
         ("gate_up_swiglu_quant", lambda: w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0,
-                                                                     dst_row=row1, workspace=gu_ws),
+                                                                     workspace=gu_ws),
          2.0 * T * k * 2 * I * H),
-        ("down_combine", lambda: w8.moe_down_combine(hq, hs, perm1, off1, tw, q2, s2, out=out, acc=acc),
+        ("down_combine", lambda: w8.moe_down_combine(hq, hs, perm0, off0, ids, tw, q2, s2, order=0, out=out, y=y),
          2.0 * T * k * H * I),
     ):
         ev = _events(reps)

@@ -141,10 +141,8 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
  * slots exist, both stable (increasing slot index inside a group):
  *   order 0, expert-major:        E groups, group of slot = its expert id e;
  *   order 1, slot-position-major: topk * E groups, group = j * E + e.
- * The down projection uses order 1: it runs once per top-k position j, each
- * token occurs once per run, and the k terms of a token are accumulated
- * without atomics in the fixed order j = 0..k-1. The gate/up tiles use
- * order 0, whose groups are k times larger (less padding in partial tiles).
+ * The fused pass uses order 0, whose groups are k times larger than those
+ * of order 1 (less padding in partial tiles); every stage accepts either.
  * Limits: 1 <= E <= 1024, 1 <= topk <= 64, at most 1024 routing groups
  * (E, or topk * E in order 1), H and I positive multiples of 16,
  * T * topk, T * H and 2 * I * H below 2^31. The fused calls need I to be a
@@ -209,16 +207,19 @@ int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int
 
 /*
  * moe_down_combine — grouped down projection and router-weighted combine:
- *   y[r, :]      = h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T)
- *   out_bf16[t]  = bf16( sum over the token's valid slots of topk_w[slot] * y )
- * perm/offsets must be in order 1 (slot-position-major). The sum is float32,
- * taken in the order j = 0..topk-1 (deterministic). acc_f32 [T, H] is
- * caller-provided scratch; it is cleared by the call. A token with no valid
- * slot gets zeros.
+ *   y[slot, :]   = topk_w[slot] * h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T)
+ *                  for the slot of sorted row r (float32)
+ *   out_bf16[t]  = bf16( sum over j = 0..topk-1 with a valid id of y[t*topk + j] )
+ * The sum is float32 and always taken in the order j = 0, 1, ... (so the
+ * result does not depend on the sorted order and is deterministic).
+ * perm/offsets may be in either order (`order`); topk_ids tells the valid
+ * slots. y_f32 [T*topk, H] is caller-provided float32 scratch. A token with
+ * no valid slot gets zeros.
  */
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
-                     const float* topk_w, const uint8_t* w2_q, const float* w2_scale, uint16_t* out_bf16,
-                     float* acc_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+                     const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const float* w2_scale,
+                     uint16_t* out_bf16, float* y_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     int order, hipStream_t stream);
 
 /* Bytes of scratch w8a8_grouped_gemm needs (0 for invalid sizes). */
 size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E);
@@ -239,12 +240,10 @@ size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int6
 
 /*
  * moe_w8a8_grouped — one routed-expert pass on buffers carved from
- * `workspace`: moe_route in both orders, moe_gate_up_swiglu_quant with
- * order-0 tiles writing each h row at its order-1 row (dst_row = the
- * order-1 slot_row), then moe_down_combine on the order-1 arrays.
- * out_bf16 [T, H]. I must be a multiple of 128. Running the stack's two
- * passes is two calls, the second on quantize_per_token of the first
- * call's output.
+ * `workspace`, all in order 0: moe_route, moe_gate_up_swiglu_quant, then
+ * moe_down_combine. out_bf16 [T, H]. I must be a multiple of 128. Running
+ * the stack's two passes is two calls, the second on quantize_per_token of
+ * the first call's output.
  */
 int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const float* topk_w,
                      const uint8_t* w13_q, const float* w13_scale, const uint8_t* w2_q, const float* w2_scale,

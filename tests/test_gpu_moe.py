@@ -140,52 +140,54 @@ def test_gate_up_bf16_full_size(gate_up_cfg):
     _check_gate_up_bf16(gate_up_cfg)
 
 
-def _check_fused_requant(d, route_idx=0, sample=None, tile_order=0):
-    """h rows land in the position-major (order 1) order; the tiles follow
-    `tile_order` (0: expert-major tiles writing through dst_row, as the full
-    pass does; 1: position-major tiles, rows in place)."""
+def _check_fused_requant(d, route_idx=0, sample=None, tile_order=0, row_order=0):
+    """Fused gate/up + SwiGLU + requantisation with tiles in `tile_order` and
+    h rows in `row_order` (different orders go through dst_row = the
+    row order's slot_row). Returns (h_q, h_scale, perm, offsets) of the row
+    order."""
     dv = _dev(d)
     ids, _ = d["routes"][route_idx]
-    counts, offsets, perm, row1 = w8.moe_route(to_dev(ids), d["E"], order=1, with_slot_row=True)
-    if tile_order == 0:
-        _, off0, perm0 = w8.moe_route(to_dev(ids), d["E"], order=0)
-        hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm0, off0, dv["q13"], dv["s13"], d["k"],
-                                             order=0, dst_row=row1)
+    ids_dev = to_dev(ids)
+    _, off_r, perm_r, row_r = w8.moe_route(ids_dev, d["E"], order=row_order, with_slot_row=True)
+    if tile_order == row_order:
+        perm_t, off_t, dst = perm_r, off_r, None
     else:
-        hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, offsets, dv["q13"], dv["s13"], d["k"],
-                                             order=1)
+        _, off_t, perm_t = w8.moe_route(ids_dev, d["E"], order=tile_order)
+        dst = row_r
+    hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm_t, off_t, dv["q13"], dv["s13"], d["k"],
+                                         order=tile_order, dst_row=dst)
     torch.cuda.synchronize()
-    _, _, rp = oracle_route(ids, d["E"], 1)
-    assert np.array_equal(perm.cpu().numpy()[:rp.size], rp)
+    _, _, rp = oracle_route(ids, d["E"], row_order)
+    assert np.array_equal(perm_r.cpu().numpy()[:rp.size], rp)
     rows = np.arange(rp.size) if sample is None else np.sort(
         np.random.default_rng(1).choice(rp.size, min(sample, rp.size), replace=False))
     gu64, err = sorted_rows_gate_up(d["qx"], d["sx"], ids, rp, rows, d["q13"], d["s13"], d["k"])
     rep = check_requant(hq.cpu().numpy()[rows], hs.cpu().numpy()[rows], gu64, err)
     print("fused requant", rep, flush=True)
     record(f"moe fused swiglu+requant T={d['T']} E={d['E']} k={d['k']} I={d['I']} tiles=order{tile_order} "
-           f"rows={len(rows)}", rep)
-    return hq, hs, perm, offsets
+           f"rows=order{row_order} n={len(rows)}", rep)
+    return hq, hs, perm_r, off_r
 
 
-@pytest.mark.parametrize("tile_order", [0, 1])
-def test_fused_requant_small(small, tile_order):
-    _check_fused_requant(small, tile_order=tile_order)
+@pytest.mark.parametrize("tile_order,row_order", [(0, 0), (1, 1), (0, 1), (1, 0)])
+def test_fused_requant_small(small, tile_order, row_order):
+    _check_fused_requant(small, tile_order=tile_order, row_order=row_order)
 
 
-@pytest.mark.parametrize("tile_order", [0, 1])
-def test_fused_requant_ragged(ragged, tile_order):
+@pytest.mark.parametrize("tile_order,row_order", [(0, 0), (1, 1), (0, 1)])
+def test_fused_requant_ragged(ragged, tile_order, row_order):
     """I = 384 (three 128-column h tiles), H = 272 (a 16-byte K tail), 9 experts."""
-    _check_fused_requant(ragged, tile_order=tile_order)
+    _check_fused_requant(ragged, tile_order=tile_order, row_order=row_order)
 
 
 def test_fused_requant_gate_up_cfg(gate_up_cfg):
     _check_fused_requant(gate_up_cfg, sample=4096)
 
 
-def _check_down(d, hq, hs, perm, offsets, route_idx=0, n_tokens=None):
+def _check_down(d, hq, hs, perm, offsets, route_idx=0, n_tokens=None, order=0):
     dv = _dev(d)
     ids, tw = d["routes"][route_idx]
-    out = w8.moe_down_combine(hq, hs, perm, offsets, to_dev(tw), dv["q2"], dv["s2"])
+    out = w8.moe_down_combine(hq, hs, perm, offsets, to_dev(ids), to_dev(tw), dv["q2"], dv["s2"], order=order)
     torch.cuda.synchronize()
     T = d["T"]
     tokens = np.arange(T) if n_tokens is None else np.sort(
@@ -194,14 +196,15 @@ def _check_down(d, hq, hs, perm, offsets, route_idx=0, n_tokens=None):
                                   d["q2"], d["s2"], d["k"], tokens)
     rep = bf16_compare(bf16_bits(out)[tokens], ref64, err)
     print("down+combine", rep, flush=True)
-    record(f"moe down+combine T={d['T']} tokens={len(tokens)}", rep)
+    record(f"moe down+combine T={d['T']} order={order} tokens={len(tokens)}", rep)
     assert rep["n_bound_violations"] == 0, rep
     assert rep["frobenius"] <= 4e-3, rep
 
 
-def test_down_combine_small(small):
-    hq, hs, perm, offsets = _check_fused_requant(small)
-    _check_down(small, hq, hs, perm, offsets)
+@pytest.mark.parametrize("order", [0, 1])
+def test_down_combine_small(small, order):
+    hq, hs, perm, offsets = _check_fused_requant(small, tile_order=order, row_order=order)
+    _check_down(small, hq, hs, perm, offsets, order=order)
 
 
 def test_down_combine_ragged(ragged):
@@ -212,12 +215,27 @@ def test_down_combine_ragged(ragged):
 def test_down_combine_deterministic(small):
     dv = _dev(small)
     ids, tw = small["routes"][0]
-    _, offsets, perm = w8.moe_route(to_dev(ids), small["E"], order=1)
+    _, offsets, perm = w8.moe_route(to_dev(ids), small["E"], order=0)
     hq, hs = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, offsets, dv["q13"], dv["s13"], small["k"],
-                                         order=1)
-    outs = [bf16_bits(w8.moe_down_combine(hq, hs, perm, offsets, to_dev(tw), dv["q2"], dv["s2"])) for _ in range(3)]
+                                         order=0)
+    outs = [bf16_bits(w8.moe_down_combine(hq, hs, perm, offsets, to_dev(ids), to_dev(tw), dv["q2"], dv["s2"]))
+            for _ in range(3)]
     torch.cuda.synchronize()
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_down_combine_order_independent(small):
+    """The per-slot products and the fixed j order of the combine make the
+    output the same, bit for bit, whichever sorted order the rows are in."""
+    outs = []
+    ids, tw = small["routes"][0]
+    dv = _dev(small)
+    for order in (0, 1):
+        hq, hs, perm, offsets = _check_fused_requant(small, tile_order=order, row_order=order)
+        outs.append(bf16_bits(w8.moe_down_combine(hq, hs, perm, offsets, to_dev(ids), to_dev(tw), dv["q2"],
+                                                  dv["s2"], order=order)))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_down_combine_two_pass_cfg(two_pass_cfg):
@@ -310,4 +328,4 @@ def test_mismatched_order_is_rejected(small):
     hq = torch.zeros((small["T"] * small["k"], small["I"]), dtype=torch.uint8, device="cuda")
     hs = torch.ones(small["T"] * small["k"], dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
-        w8.moe_down_combine(hq, hs, perm0, off0, to_dev(tw), dv["q2"], dv["s2"])
+        w8.moe_down_combine(hq, hs, perm0, off0, to_dev(ids), to_dev(tw), dv["q2"], dv["s2"], order=1)

@@ -42,7 +42,7 @@ _SIGNATURES = {
     "moe_gate_up_swiglu_quant_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 3),
     "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr, ctypes.c_size_t,
                                                                           _c_ptr]),
-    "moe_down_combine": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [_c_ptr]),
+    "moe_down_combine": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
     "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "w8a8_grouped_gemm": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
     "moe_w8a8_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 5),
@@ -272,22 +272,30 @@ def moe_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk
     return h_q, h_s
 
 
-def moe_down_combine(h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out=None, acc=None):
-    """Down projection of the sorted slots and the router-weighted combine: BF16 [T, H].
+def moe_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, order: int = 0, out=None,
+                     y=None):
+    """Down projection of the sorted rows and the router-weighted combine: BF16 [T, H].
 
-    perm/offsets must come from ``moe_route(..., order=1)``."""
+    perm/offsets come from ``moe_route(..., order=order)``; ``y`` is float32
+    scratch [T*k, H] for the per-slot products."""
     import torch
 
     T, k = topk_w.shape
     E, H, I = w2_q.shape
-    _check_order(offsets, E, k, 1)
+    _check_order(offsets, E, k, order)
+    _want(topk_ids, torch.int32, 2, "topk_ids")
+    if tuple(topk_ids.shape) != (T, k):
+        raise ValueError("topk_ids and topk_w must both be [T, k]")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
-    if acc is None:
-        acc = torch.empty((T, H), dtype=torch.float32, device=h_q.device)
+    if y is None:
+        y = torch.empty((T * k, H), dtype=torch.float32, device=h_q.device)
+    if y.numel() < T * k * H or y.dtype != torch.float32:
+        raise ValueError("y must be float32 with at least T * k * H elements")
     _check("moe_down_combine", lib().moe_down_combine(
-        h_q.data_ptr(), h_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), topk_w.data_ptr(),
-        w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), acc.data_ptr(), T, H, I, E, k, _stream(h_q)))
+        h_q.data_ptr(), h_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), topk_ids.data_ptr(),
+        topk_w.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), y.data_ptr(), T, H, I, E, k,
+        order, _stream(h_q)))
     return out
 
 

@@ -196,19 +196,22 @@ int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int
 }
 
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
-                     const float* topk_w, const uint8_t* w2_q, const float* w2_scale, uint16_t* out_bf16,
-                     float* acc_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
+                     const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const float* w2_scale,
+                     uint16_t* out_bf16, float* y_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     int order, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
-  if (w8a8::route_groups(topk, E, 1) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
+  if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
+  if (!mul_ok(T * topk, H) || !mul_ok(T * topk * H, 4)) return W8A8_ERR_BAD_SHAPE;
   if (T == 0) return W8A8_OK;
-  if (any_null({h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16, acc_f32})) return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16, acc_f32}))
+  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
+    return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
     return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
-  return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_w, w2_q, w2_scale, out_bf16,
-                                                 acc_f32, T, H, I, E, topk, stream));
+  return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
+                                                 out_bf16, y_f32, T, H, I, E, topk, order, stream));
 }
 
 size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -234,7 +237,7 @@ int w8a8_grouped_gemm(const uint8_t* x_q, const float* x_scale, const int32_t* t
 }
 
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
-  if (check_moe_shape(T, H, I, E, topk) != W8A8_OK || w8a8::route_groups(topk, E, 1) > kMaxGroups) return 0;
+  if (check_moe_shape(T, H, I, E, topk) != W8A8_OK || !mul_ok(T * topk, H) || !mul_ok(T * topk * H, 4)) return 0;
   return w8a8::moe_workspace_bytes(T, H, I, E, topk);
 }
 
@@ -245,7 +248,7 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
   if (I % kFusedIMultiple != 0) return W8A8_ERR_UNSUPPORTED;
-  if (w8a8::route_groups(topk, E, 1) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
+  if (!mul_ok(T * topk, H) || !mul_ok(T * topk * H, 4)) return W8A8_ERR_BAD_SHAPE;
   if (T == 0) return W8A8_OK;
   if (any_null({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
     return W8A8_ERR_NULL_ARG;

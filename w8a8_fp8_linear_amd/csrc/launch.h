@@ -44,10 +44,13 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
                                        int64_t I, int64_t E, int64_t topk, int order, void* ws,
                                        hipStream_t stream);
 
+// y: [T*topk, H] float32 scratch (down_combine_scratch_bytes).
+size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk);
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
-                               const int32_t* offsets, const float* tw, const uint8_t* w2,
-                               const float* s2, uint16_t* out, float* acc, int64_t T, int64_t H,
-                               int64_t I, int64_t E, int64_t topk, hipStream_t stream);
+                               const int32_t* offsets, const int32_t* ids, const float* tw,
+                               const uint8_t* w2, const float* s2, uint16_t* out, float* y, int64_t T,
+                               int64_t H, int64_t I, int64_t E, int64_t topk, int order,
+                               hipStream_t stream);
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids,
                                   const uint8_t* w13, const float* s13, uint16_t* gu, int32_t* perm,

@@ -14,34 +14,33 @@
 // sums.
 //
 // Kernels
-//  * route_count / route_scatter: slots t*k+j are grouped by expert, in
-//    increasing slot order inside an expert (a stable sort), ids outside
-//    [0, E) dropped. Chunk histograms, then one wave per sub-chunk walks its
-//    slots in order; lanes holding the same expert are matched with
-//    log2(E) ballots, so each slot's rank among earlier equal ids is a
-//    popcount. No host synchronisation: every later kernel reads the
-//    offsets from device memory and derives its own tile from them.
-//  * grouped_tiled<.., GATE_UP>: like the dense tiled GEMM, with A rows
-//    gathered through the permutation (slot -> token) and the weight of the
-//    tile's expert; BF16 output in sorted order.
-//  * gate_up_swiglu_quant: one workgroup owns 64 sorted slots and all 2I
-//    gate/up columns, so each slot's h row is complete in one place. A
-//    (64 gathered token rows) is staged in LDS by direct buffer loads;
-//    each wave streams its own 64 gate + 64 matching up weight rows straight
-//    into registers and runs 32x32x64 E4M3 MFMAs. The epilogue forms
-//    h = silu(g) * u in float32, stages h in LDS, and requantises every row
-//    (amax, scale = amax / 448, correctly rounded division, E4M3 RNE).
-//  * grouped_tiled<.., DOWN>: A = the requantised rows (already sorted and
-//    contiguous), B = W2 of the tile's expert; the epilogue multiplies by
-//    the slot scale, the channel scale and the router weight, stages the
-//    tile in LDS and adds it into a float32 [T, H] accumulator. The slots
-//    are sorted by (top-k position j, expert) and the down projection runs
-//    as one launch per j: inside a launch every token occurs at most once,
-//    so the accumulation is a plain read-add-write (no atomics; float32
-//    atomics measured ~3x slower than the whole alternative), and the k
-//    terms of a token are always added in the order j = 0, 1, ..., so the
-//    result is deterministic.
-//  * finalize: float32 accumulator -> BF16 (round to nearest even).
+//  * route_count / route_scatter: slots t*k+j are grouped by expert (or by
+//    (top-k position, expert)), in increasing slot order inside a group (a
+//    stable sort), ids outside [0, E) dropped. Chunk histograms, then one
+//    wave per sub-chunk walks its slots in order; lanes holding the same key
+//    are matched with log2(G) ballots, so each slot's rank among earlier
+//    equal keys is a popcount. Optionally also the inverse map slot -> row.
+//    No host synchronisation: every later kernel reads the offsets from
+//    device memory and derives its own tile from them.
+//  * grouped_tiled: the dense tiled pipeline (WGM x WGN waves, 128-deep K
+//    steps staged global -> LDS by direct buffer loads, double-buffered,
+//    16x16x128 E4M3 MFMAs) over sorted slots, one expert per m-tile:
+//      GATE_UP    A rows gathered through the permutation (slot -> token),
+//                 BF16 gate/up output in sorted order;
+//      GATE_UP_H  the same product with gate and up weight blocks
+//                 interleaved in the tile, so the epilogue forms
+//                 h = silu(g) * u in float32 in registers, stores h and
+//                 folds each row's max |h| into an integer atomicMax;
+//      DOWN_Y     A = the requantised rows (sorted, contiguous), B = W2 of
+//                 the tile's expert; the epilogue applies the row scale, the
+//                 channel scale and the router weight and stores the slot's
+//                 float32 product y to its own row.
+//  * requant_rows: elementwise E4M3 requantisation of h once the row maxima
+//    are known (scale = amax / 448, correctly rounded division, RNE).
+//  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots, added
+//    in the fixed order j = 0, 1, ... (deterministic, no atomics; float32
+//    atomics measured ~3x slower than this whole stage). The k rows of a
+//    token are contiguous, so this is one streaming pass.
 #include <algorithm>
 
 #include "device.h"
@@ -235,7 +234,7 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
   return false;
 }
 
-enum { kGateUp = 0, kDown = 1, kGateUpH = 2 };
+enum { kGateUp = 0, kGateUpH = 1, kDownY = 2 };
 
 template <int BM, int BN, int WGM, int WGN, int MODE>
 struct Grouped {
@@ -256,17 +255,17 @@ struct Grouped {
 };
 
 struct GroupedArgs {
-  const uint8_t* A;         // GATE_UP*: x codes [a_rows, K]; DOWN: sorted h codes [a_rows, K]
-  const float* sA;          // GATE_UP*: token scales; DOWN: sorted row scales
+  const uint8_t* A;         // GATE_UP*: x codes [a_rows, K]; DOWN_Y: sorted h codes [a_rows, K]
+  const float* sA;          // GATE_UP*: token scales; DOWN_Y: sorted row scales
   int64_t a_rows;           // rows of A (tokens, or sorted rows)
   const int32_t* perm;      // sorted row -> slot
   const int32_t* offsets;   // [G + 1] group starts (device)
   int G, Eids, topk;        // groups, experts (group g uses expert g % Eids), top-k
   const uint8_t* B;         // [E, N, K] weight codes
   const float* sB;          // [E, N] weight row scales
-  const float* tw;          // DOWN: router weights [slots]
+  const float* tw;          // DOWN_Y: router weights [slots]
   uint16_t* out_bf16;       // GATE_UP: [rows, N]
-  float* out_f32;           // GATE_UP_H: h [rows, N / 2]; DOWN: accumulator [T, N]
+  float* out_f32;           // GATE_UP_H: h [rows, N / 2]; DOWN_Y: y [slots, N]
   uint32_t* row_amax;       // GATE_UP_H: max |h| bits per output row (cleared by the caller)
   const int32_t* dst_row;   // GATE_UP_H: slot -> output row (NULL: the sorted row itself)
   int N, K, tiles_n, tiles_m_max;
@@ -286,10 +285,10 @@ struct GroupedArgs {
 //             dst_row[slot] (or r) of out_f32 [*, N/2], and posts the row's
 //             partial max |h| with an integer atomicMax on the float bits
 //             (order-independent, so the row maximum is exact).
-//  DOWN:      A row = h codes of sorted row r (contiguous); the epilogue adds
-//             w[slot] * sA[r] * sB[e, n] * acc to out_f32[token, n] straight
-//             from registers, a lane owning 4 consecutive columns of a row.
-//             The caller guarantees that a token occurs at most once per launch.
+//  DOWN_Y:    A row = h codes of sorted row r (contiguous); the epilogue
+//             stores w[slot] * sA[r] * sB[e, n] * acc to row `slot` of
+//             out_f32 [T * topk, N] straight from registers, a lane owning 4
+//             consecutive columns of a row (every slot is written once).
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
@@ -309,7 +308,8 @@ void grouped_tiled(const GroupedArgs p) {
   int t = blockIdx.x;
   if ((int)blockIdx.x < (per << 3)) t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   const int mt = t / p.tiles_n, nt = t - mt * p.tiles_n;
-  const int cap = (int)(MODE != kDown ? p.a_rows * p.topk : p.a_rows);  // sorted-row capacity
+  constexpr bool kIsDown = MODE == kDownY;
+  const int cap = (int)(kIsDown ? p.a_rows : p.a_rows * p.topk);  // sorted-row capacity
   int grp, row0, rows;
   if (!find_tile(p.offsets, p.G, BM, mt, cap, grp, row0, rows)) return;
   const int e = grp % p.Eids;
@@ -321,8 +321,8 @@ void grouped_tiled(const GroupedArgs p) {
     if (i < rows) {
       const int slot = p.perm[row0 + i];
       if (slot >= 0 && slot < cap) {
-        tok = slot / p.topk;
-        sc = MODE != kDown ? p.sA[tok] : p.sA[row0 + i] * p.tw[slot];
+        tok = MODE == kDownY ? slot : slot / p.topk;  // DOWN_Y keeps the slot: its output row
+        sc = kIsDown ? p.sA[row0 + i] * p.tw[slot] : p.sA[tok];
         if (MODE == kGateUpH) {
           dst = p.dst_row ? p.dst_row[slot] : row0 + i;
           if (dst >= cap) dst = -1;
@@ -337,8 +337,7 @@ void grouped_tiled(const GroupedArgs p) {
 
   const auto rB = MODE == kGateUpH ? make_rsrc(p.B + (int64_t)e * N * K, (int64_t)N * K)
                                     : make_rsrc(p.B + ((int64_t)e * N + n0) * K, (int64_t)(N - n0) * K);
-  const auto rA = MODE != kDown ? make_rsrc(p.A, p.a_rows * K)
-                                : make_rsrc(p.A + (int64_t)row0 * K, (int64_t)rows * K);
+  const auto rA = kIsDown ? make_rsrc(p.A + (int64_t)row0 * K, (int64_t)rows * K) : make_rsrc(p.A, p.a_rows * K);
   // Loader (as in the dense kernel): LDS slot tid + kThreads * i holds stage
   // row (tid >> 3) + kRowsPerPass * i, logical chunk (tid & 7) ^ (row & 7).
   // Stage rows 0..BN-1 hold B, rows BN.. hold A.
@@ -358,7 +357,7 @@ void grouped_tiled(const GroupedArgs p) {
 #pragma unroll
   for (int j = 0; j < C::kLoadsA; ++j) {
     const int lr = lrow + C::kRowsPerPass * j;
-    if (MODE != kDown) {
+    if (!kIsDown) {
       const int tok = row_tok[lr];
       aoff[j] = tok < 0 ? kOutOfRange : (uint32_t)tok * (uint32_t)K + (uint32_t)lchunk;
     } else {
@@ -415,36 +414,22 @@ void grouped_tiled(const GroupedArgs p) {
 
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
-  if (MODE == kDown) {
-    int toks[C::SM];
-    float rs[C::SM];
+  if (MODE == kDownY) {
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
-      toks[j] = row_tok[ml];
-      rs[j] = row_scale[ml];
-    }
+      const int slot = row_tok[ml];
+      if (slot < 0) continue;
+      const float s = row_scale[ml];
+      float* yrow = p.out_f32 + (int64_t)slot * N;
 #pragma unroll
-    for (int i = 0; i < C::SN; ++i) {
-      const int n = n0 + wn * C::WN + i * 16 + 4 * g;
-      if (n >= N) continue;
-      const float4 sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n);
-      float4 cur[C::SM];
-#pragma unroll
-      for (int j = 0; j < C::SM; ++j)
-        cur[j] = toks[j] >= 0 ? *reinterpret_cast<const float4*>(p.out_f32 + (int64_t)toks[j] * N + n)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int j = 0; j < C::SM; ++j) {
-        if (toks[j] < 0) continue;
+      for (int i = 0; i < C::SN; ++i) {
+        const int n = n0 + wn * C::WN + i * 16 + 4 * g;
+        if (n >= N) continue;
+        const float4 sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n);
         const v4f a = acc[i][j];
-        const float s = rs[j];
-        float4 c = cur[j];
-        c.x += a[0] * s * sW.x;
-        c.y += a[1] * s * sW.y;
-        c.z += a[2] * s * sW.z;
-        c.w += a[3] * s * sW.w;
-        *reinterpret_cast<float4*>(p.out_f32 + (int64_t)toks[j] * N + n) = c;
+        *reinterpret_cast<float4*>(yrow + n) =
+            make_float4(a[0] * s * sW.x, a[1] * s * sW.y, a[2] * s * sW.z, a[3] * s * sW.w);
       }
     }
     return;
@@ -551,36 +536,46 @@ __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, i
   if (i < n) p[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void fill_zero_f32(float* __restrict__ p, int64_t n4) {
+// out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots,
+// added in the order j = 0, 1, ... in float32 (deterministic). One thread
+// per 8 columns; the k rows of a token are contiguous in y.
+__global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y, const int32_t* __restrict__ ids,
+                                                     int64_t T, int topk, int Eids, int H,
+                                                     uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-__global__ __launch_bounds__(256) void finalize_bf16(const float* __restrict__ acc, uint16_t* __restrict__ out,
-                                                     int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-  const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
+  const int per_row = H >> 3;
+  const int64_t t = i / per_row;
+  if (t >= T) return;
+  const int c0 = (int)(i - t * per_row) << 3;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+  for (int j = 0; j < topk; ++j) {
+    const int64_t slot = t * topk + j;
+    const int id = ids[slot];
+    if (id < 0 || id >= Eids) continue;
+    const float4* src = reinterpret_cast<const float4*>(y + slot * H + c0);
+    const float4 u = src[0], v = src[1];
+    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+  }
   uint4 o;
   o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
   o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
   o.z = f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16);
   o.w = f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16);
-  reinterpret_cast<uint4*>(out)[i] = o;
+  *reinterpret_cast<uint4*>(out + t * H + c0) = o;
 }
 
 int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
 int route_chunks(int64_t n) { return (int)((n + kRouteChunk - 1) / kRouteChunk); }
 
-// Tile shapes. The gate/up runs on expert-major groups (about T*k/E rows
-// each): 256 x 256 tiles, 8 waves of 128 x 64. The down projection runs once
-// per top-k position on groups of about T/E rows: 128 x 128 tiles, 4 waves,
-// two workgroups per CU so that one's read-add-write epilogue overlaps the
-// other's MFMAs.
+// Tile shapes (both on expert-major groups of about T*k/E rows): 256 x 256
+// tiles, 8 waves of 128 x 64, two waves per SIMD. Measured on the 16384-token
+// two-pass workload against 128 x 256 (8 waves) and 128 x 128 (4 waves, two
+// workgroups per CU) for the down projection, and 128 x 256 and 4 x 2 waves
+// for the gate/up: this shape was the fastest or within noise for both.
 constexpr int kGuBM = 256, kGuBN = 256, kGuWGM = 2, kGuWGN = 4, kGuOcc = 2;
-constexpr int kDnBM = 128, kDnBN = 128, kDnWGM = 2, kDnWGN = 2, kDnOcc = 2;
+constexpr int kDnBM = 256, kDnBN = 256, kDnWGM = 2, kDnWGN = 4, kDnOcc = 2;
 
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
@@ -672,63 +667,57 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
   return hipGetLastError();
 }
 
-// Needs the slot-position-major order (order = 1): launch j covers groups
-// [j * E, (j + 1) * E), in which every token occurs at most once.
+// Down projection of the sorted rows (any order: every slot's product goes
+// to its own row of y), then the per-token combine.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm, const int32_t* offsets,
-                               const float* tw, const uint8_t* w2, const float* s2, uint16_t* out, float* acc,
-                               int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, hipStream_t stream) {
-  const int64_t n4 = T * H / 4;
-  hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, acc, n4);
+                               const int32_t* ids, const float* tw, const uint8_t* w2, const float* s2, uint16_t* out,
+                               float* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
+                               hipStream_t stream) {
   GroupedArgs a{};
   a.A = qh;
   a.sA = sh;
   a.a_rows = T * topk;
   a.perm = perm;
-  a.G = (int)E;
+  a.offsets = offsets;
+  a.G = (int)route_groups(topk, E, order);
   a.Eids = (int)E;
   a.topk = (int)topk;
   a.B = w2;
   a.sB = s2;
   a.tw = tw;
-  a.out_f32 = acc;
+  a.out_f32 = y;
   a.N = (int)H;
   a.K = (int)I;
-  for (int64_t j = 0; j < topk; ++j) {
-    a.offsets = offsets + j * E;
-    const hipError_t err = run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, kDown, kDnOcc>(a, T, stream);
-    if (err != hipSuccess) return err;
-  }
-  const int64_t n8 = T * H / 8;
-  hipLaunchKernelGGL(finalize_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, acc, out, n8);
+  const hipError_t err = run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, kDownY, kDnOcc>(a, T * topk, stream);
+  if (err != hipSuccess) return err;
+  const int64_t threads = T * (H / 8);
+  hipLaunchKernelGGL(combine_slots, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, y, ids, T,
+                     (int)topk, (int)E, (int)H, out);
   return hipGetLastError();
 }
 
+size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk) { return (size_t)(T * topk * H * 4); }
+
 // Workspace of the full pass:
-//   counts0 | offsets0 | perm0          expert-major routing (gate/up tiles)
-//   counts1 | offsets1 | perm1 | row1   position-major routing (down launches)
-//   route scratch | qh | sh | amax | big
-// where big holds h [T*k, I] float32 during the gate/up and then the float32
-// [T, H] accumulator of the down projection.
+//   counts | offsets | perm | route scratch | qh | sh | amax | big
+// where big holds h [T*k, I] float32 during the gate/up and then the
+// weighted slot products y [T*k, H] float32 of the down projection.
 struct MoeLayout {
-  int64_t counts0, offsets0, perm0, counts1, offsets1, perm1, row1, route, qh, sh, amax, big, total;
+  int64_t counts, offsets, perm, route, qh, sh, amax, big, total;
 };
 
 static MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
   MoeLayout L;
   int64_t o = 0;
-  const int64_t n = T * topk, G1 = route_groups(topk, E, 1);
-  L.counts0 = o; o += align256(E * 4);
-  L.offsets0 = o; o += align256((E + 1) * 4);
-  L.perm0 = o; o += align256(n * 4);
-  L.counts1 = o; o += align256(G1 * 4);
-  L.offsets1 = o; o += align256((G1 + 1) * 4);
-  L.perm1 = o; o += align256(n * 4);
-  L.row1 = o; o += align256(n * 4);
-  L.route = o; o += (int64_t)route_workspace_bytes(T, topk, G1);
+  const int64_t n = T * topk;
+  L.counts = o; o += align256(E * 4);
+  L.offsets = o; o += align256((E + 1) * 4);
+  L.perm = o; o += align256(n * 4);
+  L.route = o; o += (int64_t)route_workspace_bytes(T, topk, E);
   L.qh = o; o += align256(n * I);
   L.sh = o; o += align256(n * 4);
   L.amax = o; o += align256(n * 4);  // amax | big is the gate/up stage's workspace
-  L.big = o; o += std::max(align256(n * I * 4), align256(T * H * 4));
+  L.big = o; o += std::max(align256(n * I * 4), align256(n * H * 4));
   L.total = o;
   return L;
 }
@@ -737,28 +726,25 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t t
   return (size_t)moe_layout(T, H, I, E, topk).total;
 }
 
-// One pass: the gate/up tiles follow the expert-major order (large groups,
-// each expert's weights streamed once per 256 rows) and write each h row at
-// its position-major row, which the down launches then read contiguously.
+// One pass, all on the expert-major order: route, gate/up + SwiGLU +
+// requantisation, down projection into per-slot rows, combine.
 hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, const float* tw, const uint8_t* w13,
                       const float* s13, const uint8_t* w2, const float* s2, uint16_t* out, int64_t T, int64_t H,
                       int64_t I, int64_t E, int64_t topk, void* ws, hipStream_t stream) {
   const MoeLayout L = moe_layout(T, H, I, E, topk);
   uint8_t* b = static_cast<uint8_t*>(ws);
-  auto i32 = [&](int64_t off) { return reinterpret_cast<int32_t*>(b + off); };
-  hipError_t err = launch_route(ids, T, topk, E, 0, i32(L.counts0), i32(L.offsets0), i32(L.perm0), nullptr,
-                                b + L.route, stream);
-  if (err != hipSuccess) return err;
-  err = launch_route(ids, T, topk, E, 1, i32(L.counts1), i32(L.offsets1), i32(L.perm1), i32(L.row1), b + L.route,
-                     stream);
-  if (err != hipSuccess) return err;
+  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(b + L.perm);
   uint8_t* qh = b + L.qh;
   float* sh = reinterpret_cast<float*>(b + L.sh);
-  err = launch_gate_up_swiglu_quant(xq, xs, i32(L.perm0), i32(L.offsets0), i32(L.row1), w13, s13, qh, sh, T, H, I, E,
-                                    topk, 0, b + L.amax, stream);
+  hipError_t err = launch_route(ids, T, topk, E, 0, counts, offsets, perm, nullptr, b + L.route, stream);
   if (err != hipSuccess) return err;
-  return launch_down_combine(qh, sh, i32(L.perm1), i32(L.offsets1), tw, w2, s2, out,
-                             reinterpret_cast<float*>(b + L.big), T, H, I, E, topk, stream);
+  err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, T, H, I, E, topk, 0,
+                                    b + L.amax, stream);
+  if (err != hipSuccess) return err;
+  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<float*>(b + L.big), T, H,
+                             I, E, topk, 0, stream);
 }
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids, const uint8_t* w13,
