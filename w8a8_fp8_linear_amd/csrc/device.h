@@ -78,6 +78,26 @@ __device__ inline uint32_t e4m3_rne_sat(float v) {
   return code | sign;
 }
 
+// Four float32 values in [-448, 448] -> four E4M3 codes (value 0 in byte 0)
+// with the hardware conversion (round to nearest even). Verified on gfx950 to
+// equal e4m3_rne_sat for every float32 bit pattern of magnitude <= 448.
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ inline float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// True when the E4M3 code of a float32 within 2 ulp of v may differ from
+// that of v: v lies within 3 ulp of a round-to-nearest boundary of the
+// normal E4M3 range (the 20 bits below the kept mantissa are near one half),
+// or 0 < |v| < 2^-6 (the subnormal range, whose boundaries sit elsewhere).
+__device__ inline bool e4m3_boundary_near(float v) {
+  const uint32_t a = __float_as_uint(v) & 0x7FFFFFFFu;
+  return (a - 1u < 0x3C7FFFFFu) | (((a & 0xFFFFFu) - 0x7FFFDu) < 7u);
+}
+
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {

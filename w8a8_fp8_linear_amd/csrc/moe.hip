@@ -506,7 +506,10 @@ void grouped_tiled(const GroupedArgs p) {
 
 // Requantisation of float32 h rows, elementwise once the row maxima are
 // known: s_r = fl32(amax_r / 448) (1 for an all-zero row), q = E4M3(fl32(h / s_r))
-// (IEEE division, round to nearest even, saturating). One thread per 16
+// (round to nearest even, saturating). As in the activation quantiser, h * r
+// with r = fl32(1 / s_r) stands in for the correctly rounded quotient unless
+// it lies within a few ulp of an E4M3 rounding boundary (or below 2^-6),
+// where the thread redoes its values with the division. One thread per 16
 // values of a row; rows from the valid count on are left alone.
 __global__ __launch_bounds__(256) void requant_rows(const float* __restrict__ h, const uint32_t* __restrict__ amax_bits,
                                                     const int32_t* __restrict__ nvalid, int64_t cap, int I,
@@ -519,15 +522,29 @@ __global__ __launch_bounds__(256) void requant_rows(const float* __restrict__ h,
   const int c0 = (int)(i - row * per_row) << 4;
   const float amax = __uint_as_float(amax_bits[row]);
   const float s = amax == 0.f ? 1.0f : amax / 448.0f;
+  const float r = 1.0f / s;
   const float4* src = reinterpret_cast<const float4*>(h + row * I + c0);
-  uint32_t w[4];
+  float x[16], q[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 v = src[q];
-    w[q] = e4m3_rne_sat(v.x / s) | (e4m3_rne_sat(v.y / s) << 8) | (e4m3_rne_sat(v.z / s) << 16) |
-           (e4m3_rne_sat(v.w / s) << 24);
+  for (int k = 0; k < 4; ++k) {
+    const float4 v = src[k];
+    x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
   }
-  *reinterpret_cast<uint4*>(qh + row * I + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+  bool near = !(r < 3.0e38f);  // a subnormal scale: 1 / s overflows, divide everything
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    q[k] = x[k] * r;
+    near |= e4m3_boundary_near(q[k]);
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q[k] = x[k] / s;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) q[k] = clamp448(q[k]);
+  *reinterpret_cast<uint4*>(qh + row * I + c0) =
+      make_uint4(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]), e4m3x4(q[8], q[9], q[10], q[11]),
+                 e4m3x4(q[12], q[13], q[14], q[15]));
   if (c0 == 0) sh[row] = s;
 }
 

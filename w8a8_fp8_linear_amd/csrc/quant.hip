@@ -10,7 +10,14 @@
 //
 // One wave per row: BF16 is read with 16-byte loads (8 values per lane per
 // load) and kept in registers, amax is a wave-wide max, then every element
-// is divided by s with a correctly rounded float32 division and encoded.
+// is scaled and encoded. fl32(x / s) is obtained without a division per
+// element: v = x * r with r = fl32(1 / s) is within 2 ulp of fl32(x / s)
+// (two roundings of relative size 2^-24 each), so v and fl32(x / s) have the
+// same E4M3 code unless v is within a few ulp of a rounding boundary or in
+// the subnormal range; a lane holding such a value redoes its 8 values with
+// the correctly rounded division (so does every lane of a row whose scale is
+// so small that 1 / s overflows). The encoding itself is the hardware
+// conversion (round to nearest even) after clamping to +-448.
 // Rows longer than 64 * 8 * 16 values stream through twice instead.
 #include "device.h"
 #include "launch.h"
@@ -32,19 +39,30 @@ __device__ inline uint32_t absmax8(uint4 v) {
   return m;
 }
 
-// 8 BF16 values -> 8 E4M3 codes (little-endian, element 0 in byte 0).
-__device__ inline uint2 quant8(uint4 v, float s) {
+// 8 BF16 values -> 8 E4M3 codes of fl32(x / s) (little-endian, element 0 in
+// byte 0); r = fl32(1 / s), or a non-finite r (a subnormal scale) to divide
+// every value.
+__device__ inline uint2 quant8(uint4 v, float s, float r) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t c[8];
+  float x[8], q[8];
+  bool near = !(r < 3.0e38f);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    c[2 * i] = e4m3_rne_sat(bf16_lo(w[i]) / s);
-    c[2 * i + 1] = e4m3_rne_sat(bf16_hi(w[i]) / s);
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
   }
-  uint2 r;
-  r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-  return r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    q[k] = x[k] * r;
+    near |= e4m3_boundary_near(q[k]);
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = x[k] / s;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q[k] = clamp448(q[k]);
+  return make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
 }
 
 __device__ inline float row_scale(uint32_t amax_bits) {
@@ -77,11 +95,12 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
   }
   amax = wave_max_u32(amax);
   const float s = row_scale(amax);
+  const float r = 1.0f / s;
   uint2* qr = reinterpret_cast<uint2*>(q + row * K);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) qr[c] = quant8(v[i], s);
+    if (c < nch) qr[c] = quant8(v[i], s, r);
   }
   if (lane == 0) scale[row] = s;
 }
@@ -101,8 +120,9 @@ __global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restr
   }
   amax = wave_max_u32(amax);
   const float s = row_scale(amax);
+  const float r = 1.0f / s;
   uint2* qr = reinterpret_cast<uint2*>(q + row * K);
-  for (int64_t c = lane; c < nch; c += 64) qr[c] = quant8(xr[c], s);
+  for (int64_t c = lane; c < nch; c += 64) qr[c] = quant8(xr[c], s, r);
   if (lane == 0) scale[row] = s;
 }
 
