@@ -40,6 +40,16 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+# HBM bytes per launch of the prefill GEMM kernel, from two rocprofv3 counter
+# passes over `bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-decode
+# --no-moe --copy-calibration` (profiles/gemm_prefill_hbm_counters.md):
+# FETCH_SIZE 41,097 KiB per dispatch, scaled by 2 because the same counter
+# reads 131,089 KiB for the 256 MiB device copy; WRITE_SIZE 49,152 KiB, scale 1
+# (the copy's 262,144 KiB). Valid for this kernel only; None for any other.
+GEMM_PREFILL_TRAFFIC = {"kernel": "gemm_tiled<256,192,2,4>", "bytes": (41097 * 2 + 49152) * 1024}
+GEMM_PREFILL_KERNEL = "gemm_tiled<256,192,2,4>"
+
+
 def bench_prefill(steps, warmup):
     import torch
 
@@ -56,34 +66,37 @@ def bench_prefill(steps, warmup):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step():
         w8.quantize_per_token(x, xq, xs)
-        if ev is not None:
-            ev[0].record(stream)
         w8.w8a8_gemm(xq, xs, wq, ws, out=y)
-        if ev is not None:
-            ev[1].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
+    for _ in range(steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gemm_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    gemm_avg = sum(gemm_ms) / len(gemm_ms)
 
-    # quantiser alone, same stream, event-timed
-    qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in qe:
-        a.record(stream)
-        w8.quantize_per_token(x, xq, xs)
-        b.record(stream)
-    torch.cuda.synchronize()
-    q_avg = sum(a.elapsed_time(b) for a, b in qe) / steps
+    # Each kernel's average launch duration: `steps` back-to-back launches on
+    # the same stream between two HIP events, repeated `rounds` times.
+    def launches_ms(fn, rounds=5):
+        out = []
+        for _ in range(rounds):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / steps)
+        return sorted(out)
+
+    gemm_ms = launches_ms(lambda: w8.w8a8_gemm(xq, xs, wq, ws, out=y))
+    gemm_avg = sum(gemm_ms) / len(gemm_ms)
+    q_ms = launches_ms(lambda: w8.quantize_per_token(x, xq, xs))
+    q_avg = sum(q_ms) / len(q_ms)
 
     flops = 2.0 * M * N * K
     gemm_bytes = M * K + N * K + 2 * M * N + 4 * (M + N)
@@ -91,8 +104,7 @@ def bench_prefill(steps, warmup):
     return {
         "M": M, "N": N, "K": K, "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
         "tflops": flops * steps / wall / 1e12,
-        "gemm_ms_avg": gemm_avg, "gemm_ms_p10": gemm_ms[len(gemm_ms) // 10],
-        "gemm_ms_p90": gemm_ms[(9 * len(gemm_ms)) // 10],
+        "gemm_ms_avg": gemm_avg, "gemm_ms_min": gemm_ms[0], "gemm_ms_max": gemm_ms[-1],
         "gemm_tflops": flops / (gemm_avg * 1e-3) / 1e12, "gemm_flops": flops, "gemm_bytes": gemm_bytes,
         "quant_ms_avg": q_avg, "quant_gbs": q_bytes / (q_avg * 1e-3) / 1e9, "quant_bytes": q_bytes,
         "tokens_per_s": M * steps / wall,
@@ -108,8 +120,6 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
     cfg = synth.DENSE_DECODE
     N, K = cfg["N"], cfg["K"]
     # distinct weight buffers: 40 x 16.8 MB = 671 MB, more than the last-level cache
-    g = torch.Generator(device="cuda")
-    g.manual_seed(0)
     wqs, wss = [], []
     d = synth.dense_workload(M=1, K=K, N=N, seed=0)
     wq0, ws0 = w8.quantize_weight(_bf16_dev(d["w"]))
@@ -126,25 +136,57 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
         for i in range(n_buffers):
             w8.w8a8_gemm(xq, xs, wqs[i], wss[i], out=y)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n_buffers * reps)]
-        t0 = time.perf_counter()
-        for j, (a, b) in enumerate(evs):
-            a.record(stream)
-            w8.w8a8_gemm(xq, xs, wqs[j % n_buffers], wss[j % n_buffers], out=y)
-            b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = sorted(a.elapsed_time(b) for a, b in evs)
-        avg = sum(ms) / len(ms)
+        # The n_buffers launches (each on the next weight buffer) are captured
+        # once into a HIP graph and the graph is replayed between two events:
+        # at ~6 us per kernel the Python launch path would otherwise be the
+        # bottleneck. Without graph support, plain back-to-back launches.
+        launches = [lambda j=j: w8.w8a8_gemm(xq, xs, wqs[j], wss[j], out=y) for j in range(n_buffers)]
+        rounds, method = _per_launch_ms(launches, reps, stream)
+        avg = sum(rounds) / len(rounds)
         wbytes = N * K + 4 * N
         out[f"M{M}"] = {
-            "kernel_us_avg": 1e3 * avg, "kernel_us_p50": 1e3 * ms[len(ms) // 2],
+            "kernel_us_avg": 1e3 * avg, "kernel_us_min_max_of_rounds": [1e3 * rounds[0], 1e3 * rounds[-1]],
+            "timing": method,
             "weight_stream_GBs": wbytes / (avg * 1e-3) / 1e9,
             "frac_hbm_peak": wbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "wall_us_per_call": 1e6 * wall / len(evs), "weight_bytes": wbytes,
+            "weight_bytes": wbytes,
         }
     return out
+
+
+def _per_launch_ms(launches, reps, stream):
+    """Average time per launch of `launches` (a list of callables), per round of `reps`."""
+    import torch
+
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in launches:
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        rounds = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            rounds.append(a.elapsed_time(b) / len(launches))
+        del g
+        return sorted(rounds), "hip graph replay of back-to-back launches"
+    except RuntimeError:
+        torch.cuda.synchronize()
+    rounds = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for fn in launches:
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        rounds.append(a.elapsed_time(b) / len(launches))
+    return sorted(rounds), "back-to-back launches"
 
 
 def _events(n):
@@ -357,11 +399,14 @@ def main():
         "data": "synthetic (seeded N(0,1) activations with 1% x20 outlier channels, N(0,0.02) weights)",
         "config": {"workload": "prefill projection 4096 tokens x 2048 -> 6144 (per-token quant + W8A8 GEMM)",
                    "M": pre["M"], "N": pre["N"], "K": pre["K"]},
-        "roofline": {"bound": "mfma", "kernel": "gemm_tiled<256,192,2,4>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": GEMM_PREFILL_KERNEL, "achieved": round(achieved, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": (GEMM_PREFILL_TRAFFIC["bytes"]
+                                 if GEMM_PREFILL_TRAFFIC["kernel"] == GEMM_PREFILL_KERNEL else None),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes": pre["gemm_bytes"]},
         "gemm_us_avg": round(pre["gemm_ms_avg"] * 1e3, 3),
-        "gemm_us_p10_p90": [round(pre["gemm_ms_p10"] * 1e3, 3), round(pre["gemm_ms_p90"] * 1e3, 3)],
+        "gemm_us_min_max_of_rounds": [round(pre["gemm_ms_min"] * 1e3, 3), round(pre["gemm_ms_max"] * 1e3, 3)],
         "quant_us_avg": round(pre["quant_ms_avg"] * 1e3, 3),
         "quant_GBs": round(pre["quant_gbs"], 1),
         "tokens_per_s": round(pre["tokens_per_s"], 1),

@@ -565,14 +565,26 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
   if (t >= T) return;
   const int c0 = (int)(i - t * per_row) << 3;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  for (int j = 0; j < topk; ++j) {
-    const int64_t slot = t * topk + j;
-    const int id = ids[slot];
-    if (id < 0 || id >= Eids) continue;
-    const float4* src = reinterpret_cast<const float4*>(y + slot * H + c0);
-    const float4 u = src[0], v = src[1];
-    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
-    b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+  constexpr int kBatch = 8;  // rows loaded before any is added (a dropped slot's row is read but not used)
+  for (int j0 = 0; j0 < topk; j0 += kBatch) {
+    float4 u[kBatch], v[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int j = j0 + jj;
+      const int64_t slot = t * topk + (j < topk ? j : 0);
+      const int id = ids[slot];
+      ok[jj] = j < topk && id >= 0 && id < Eids;
+      const float4* src = reinterpret_cast<const float4*>(y + slot * H + c0);
+      u[jj] = src[0];
+      v[jj] = src[1];
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      if (!ok[jj]) continue;
+      a.x += u[jj].x; a.y += u[jj].y; a.z += u[jj].z; a.w += u[jj].w;
+      b.x += v[jj].x; b.y += v[jj].y; b.z += v[jj].z; b.w += v[jj].w;
+    }
   }
   uint4 o;
   o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
