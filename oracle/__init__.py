@@ -18,6 +18,10 @@ What it defines, and where the pages state it:
   --fast-math does"); the weights are decoded exactly and the product is
   carried out in high precision, the emulation the same page's
   "Benchmarks" section describes for its FP8 scores.
+* The default-maths linear (``linear.w8a16_linear``): without the fast-math
+  flag the FP8 weights are widened to 16 bits and the product is taken in
+  BF16 on unquantised activations (Lernex/Metis-1.6-Logos-FP8, "What
+  --fast-math does").
 * The routed-expert chain (``moe``): routed experts in FP8 with the same
   scheme, top-k routing, the stack run twice with shared weights
   (Lernex/Metis-1.6-Praxis, "Architecture"; sglang-metis 0.1.0, "How the
@@ -32,12 +36,12 @@ from .e4m3 import (E4M3_MAX, decode, decode_table, encode, encode_bits,
                    finite_codes, magnitudes)
 from .bf16 import bf16_bits_to_f64, round_to_bf16_bits
 from .quant import bf16_bits_to_f32, quantize_rows
-from .linear import w8a8_linear, w8a8_linear_int
+from .linear import w8a8_linear, w8a8_linear_int, w8a16_linear
 from .moe import (route, grouped_gate_up, moe_pass, moe_two_pass, swiglu_f32)
 
 __all__ = [
     "E4M3_MAX", "decode", "decode_table", "encode", "encode_bits", "finite_codes", "magnitudes",
     "bf16_bits_to_f64", "round_to_bf16_bits", "bf16_bits_to_f32", "quantize_rows",
-    "w8a8_linear", "w8a8_linear_int", "route", "grouped_gate_up", "moe_pass", "moe_two_pass",
+    "w8a8_linear", "w8a8_linear_int", "w8a16_linear", "route", "grouped_gate_up", "moe_pass", "moe_two_pass",
     "swiglu_f32",
 ]

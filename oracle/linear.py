@@ -25,10 +25,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bf16 import round_to_bf16_bits
+from .bf16 import bf16_bits_to_f64, round_to_bf16_bits
 from .e4m3 import decode
 
-__all__ = ["w8a8_linear", "w8a8_linear_int", "dequant_sum"]
+__all__ = ["w8a8_linear", "w8a8_linear_int", "dequant_sum", "w8a16_linear"]
 
 
 def dequant_sum(qa, qb) -> np.ndarray:
@@ -68,3 +68,24 @@ def w8a8_linear_int(qx, qw) -> np.ndarray:
     a = _code_to_int512(qx)
     b = _code_to_int512(qw)
     return a @ b.T
+
+
+def w8a16_linear(x_bits, qw, sw):
+    """The default maths: BF16 activations times the exactly decoded weights.
+
+    Lernex/Metis-1.6-Logos-FP8, "What --fast-math does": without the flag the
+    FP8 weights are widened to 16 bits and the product is taken in BF16, so
+    only the weights are rounded (the activations are not quantised):
+
+        Y[m, n] = bf16( s_w[n] * sum_k x[m, k] * dec(qw[n, k]) )
+
+    ``x_bits`` are BF16 bit patterns [M, K]. Returns ``(y64, y_bf16)``.
+
+    Precision: each product of a BF16 value (8 significant bits) and an E4M3
+    value (4) is exact in float64; the float64 sum differs from the exact one
+    by at most K * 2**-53 * sum |x w|, far below the BF16 output rounding.
+    """
+    x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    w = decode(np.asarray(qw, dtype=np.uint8))
+    y = (x @ w.T) * np.asarray(sw, np.float32).astype(np.float64)[None, :]
+    return y, round_to_bf16_bits(y)
