@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
 METRIC = "W8A8 TFLOP/s & % FP8 MFMA peak (prefill M=4096); HBM GB/s at decode M=8"
 
 
@@ -151,6 +152,67 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
             "frac_hbm_peak": wbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "weight_bytes": wbytes,
         }
+    return out
+
+
+def bench_default_maths(steps=50, warmup=10, Ms=(1, 8), n_buffers=40, reps=5):
+    """The default maths (W8A16) against the FP8 multiply: the model page's
+    fast-math comparison at a 4,096-token prompt, and the decode weight stream."""
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    stream = torch.cuda.current_stream()
+    cfg = synth.DENSE_PREFILL
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    d = synth.dense_workload(**cfg, seed=0)
+    x = _bf16_dev(d["x"])
+    wq, ws = w8.quantize_weight(_bf16_dev(d["w"]))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsp = torch.empty(int(w8.lib().fp8_linear_workspace_bytes(M, K)), dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, fast in (("fast_math", True), ("default", False)):
+        for _ in range(warmup):
+            w8.fp8_linear(x, wq, ws, fast_math=fast, out=y, workspace=wsp)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            w8.fp8_linear(x, wq, ws, fast_math=fast, out=y, workspace=wsp)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        out[name] = {"us_per_layer": 1e3 * ms, "tokens_per_s": M / (ms * 1e-3),
+                     "tflops": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+    w16 = [1e3 * v for v in
+           _per_launch_ms([lambda: w8.w8a16_gemm(x, wq, ws, out=y)] * steps, reps, stream)[0]]
+    out["w8a16_gemm_us"] = sum(w16) / len(w16)
+    out["w8a16_gemm_frac_bf16_peak"] = 2.0 * M * N * K / (out["w8a16_gemm_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
+    out["fast_math_speedup"] = out["default"]["us_per_layer"] / out["fast_math"]["us_per_layer"]
+    out["workload"] = "prefill projection 4096 tokens x 2048 -> 6144: fp8_linear with and without fast_math"
+    # decode: the weight stream of the default maths (what a single conversation runs)
+    dcfg = synth.DENSE_DECODE
+    Nd, Kd = dcfg["N"], dcfg["K"]
+    dd = synth.dense_workload(M=1, K=Kd, N=Nd, seed=0)
+    wq0, ws0 = w8.quantize_weight(_bf16_dev(dd["w"]))
+    wqs = [wq0.roll(i, dims=0).contiguous() for i in range(n_buffers)]
+    wss = [ws0.roll(i).contiguous() for i in range(n_buffers)]
+    dec = {}
+    for Md in Ms:
+        xd = _bf16_dev(synth.dense_workload(M=Md, K=Kd, N=Nd, seed=1)["x"])
+        yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device="cuda")
+        for j in range(n_buffers):
+            w8.w8a16_gemm(xd, wqs[j], wss[j], out=yd)
+        torch.cuda.synchronize()
+        launches = [lambda j=j: w8.w8a16_gemm(xd, wqs[j], wss[j], out=yd) for j in range(n_buffers)]
+        rounds, method = _per_launch_ms(launches, reps, stream)
+        avg = sum(rounds) / len(rounds)
+        wbytes = Nd * Kd + 4 * Nd
+        dec[f"M{Md}"] = {"kernel_us_avg": 1e3 * avg, "timing": method,
+                         "weight_stream_GBs": wbytes / (avg * 1e-3) / 1e9,
+                         "frac_hbm_peak": wbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["decode"] = dec
     return out
 
 
@@ -348,6 +410,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-default-maths", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -379,6 +442,10 @@ def main():
         moe_gu = bench_moe_gate_up()
         print("[bench] routed FFN, two passes", file=sys.stderr, flush=True)
         moe_ffn = bench_moe_two_pass()
+    dm = None
+    if not args.no_default_maths:
+        print("[bench] default maths (W8A16)", file=sys.stderr, flush=True)
+        dm = bench_default_maths()
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -413,6 +480,7 @@ def main():
         "decode": dec,
         "moe_gate_up": moe_gu,
         "moe_two_pass": moe_ffn,
+        "default_maths": dm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

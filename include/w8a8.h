@@ -114,6 +114,48 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
               uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 
+/*
+ * w8a16_gemm — the default maths: BF16 activations times the E4M3 weights
+ * widened to BF16, on the BF16 matrix units.
+ *
+ * Without the fast-math flag the model page's runtime widens the FP8 weights
+ * to 16 bits as it multiplies and does the product in BF16, so the weights
+ * are the only rounded operand (Lernex/Metis-1.6-Logos-FP8, "What --fast-math
+ * does"):
+ *   y[m,n] = bf16( w_scale[n] * sum_k x[m,k] * dec(w[n,k]) )
+ * Every E4M3 value is exact in BF16; products are exact, sums are float32,
+ * the scale is applied in float32 and the result is rounded to nearest even.
+ * No activation quantisation, no activation scale, no bias. M <= 32 runs a
+ * weight-streaming kernel; larger M a tiled one.
+ *
+ *   x_bf16   [M, K] BF16 activations
+ *   w_q      [N, K] E4M3 weights    w_scale [N] per-output-row scales
+ *   y_bf16   [M, N] output (must not overlap the inputs)
+ *   M, N, K  as for w8a8_gemm
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, DEVICE, LAUNCH.
+ */
+int w8a16_gemm(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
+               int64_t N, int64_t K, hipStream_t stream);
+
+/* Bytes of scratch fp8_linear needs on its FP8 path: M*K codes + M scales,
+ * each rounded up to 256 bytes (0 for invalid sizes). */
+size_t fp8_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * fp8_linear — the layer as the model page's runtime chooses it: with
+ * fast_math != 0 and more than 8 tokens (M > 8), quantize_per_token into the
+ * workspace followed by w8a8_gemm; otherwise w8a16_gemm. The page states that
+ * the flag changes only steps that handle many tokens at once (prompt reading,
+ * more than 8 conversations) and that a single conversation's generation uses
+ * the default maths either way (Lernex/Metis-1.6-Logos-FP8, "What --fast-math
+ * does").
+ *   workspace  fp8_linear_workspace_bytes(M, K) bytes of device scratch; only
+ *              read on the FP8 path (may be NULL otherwise)
+ * Other arguments and errors as w8a16_gemm, plus WORKSPACE.
+ */
+int fp8_linear(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
+               int64_t N, int64_t K, int fast_math, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Routed experts
  *

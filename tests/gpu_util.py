@@ -89,3 +89,42 @@ def gemm_report(got_bits, qx, sx, qw, sw, rows=None):
         "n": int(g.size),
         "rms": rms,
     }
+
+
+BF16_MFMA_ERR = 2.0 ** -20  # BF16 MFMA internal summation (measured worst 2**-21.7 * sum |terms|)
+
+
+def w8a16_report(got_bits, x_bits, qw, sw):
+    """Compare a GPU default-maths (W8A16) result with the oracle.
+
+    Element bound of the BF16 matrix-core path:
+
+        |y_gpu - y64| <= (2**-20 + (K/32 + 3) * 2**-24) * s_w sum_k |x_k w_k| + ulp_bf16(y_gpu) / 2
+
+    Products of a BF16 and an E4M3 value are exact in float32. The first
+    term is the 16x16x32 BF16 MFMA's own summation of its 32 products
+    (measured on the device at 2**-21.7 * sum |terms| at worst, taken with
+    margin); each of the K/32 instructions then adds into the float32
+    accumulator with one rounding, and the scale multiply adds one more.
+    """
+    x64 = oracle.bf16_bits_to_f64(x_bits)
+    y64, ybf = oracle.w8a16_linear(x_bits, qw, sw)
+    K = x64.shape[1]
+    absacc = np.abs(x64) @ np.abs(oracle.decode(qw)).T
+    scale = np.asarray(sw, np.float64)[None, :]
+    g = oracle.bf16_bits_to_f64(got_bits)
+    ref = oracle.bf16_bits_to_f64(ybf)
+    bound = (BF16_MFMA_ERR + (K / 32 + 3) * U32) * 1.01 * scale * absacc + 0.5 * bf16_ulp(g) + 1e-300
+    viol = np.abs(g - y64) > bound
+    rms = float(np.sqrt(np.mean(y64 ** 2)))
+    diff = np.abs(g - ref)
+    fro = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-300))
+    return {
+        "frobenius": fro,
+        "max_abs_over_rms": float(diff.max() / rms) if rms > 0 else 0.0,
+        "n_over_1e-2_rms": int((diff > 1e-2 * rms).sum()),
+        "n_differ_from_bf16_ref": int((got_bits != ybf).sum()),
+        "n_bound_violations": int(viol.sum()),
+        "n": int(g.size),
+        "rms": rms,
+    }

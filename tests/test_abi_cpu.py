@@ -81,3 +81,31 @@ def test_valid_call_without_gpu_reports_device():
         pytest.skip("a GPU is present")
     assert w8.lib().quantize_per_token(P, 4, 16, P, P, None) == DEV
     assert w8.lib().w8a8_gemm(P, P, P, P, P, 4, 16, 16, None) == DEV
+
+
+def test_w8a16_gemm_argument_errors():
+    f = w8.lib().w8a16_gemm
+    assert f(P, P, P, P, -1, 16, 16, None) == SHAPE
+    assert f(P, P, P, P, 4, 16, 8, None) == UNSUP
+    assert f(P, P, P, P, 4, 24, 16, None) == UNSUP
+    assert f(P, P, P, P, 0, 16, 16, None) == OK
+    assert f(None, P, P, P, 4, 16, 16, None) == NULL
+    assert f(P, P, None, P, 4, 16, 16, None) == NULL
+    assert f(P + 2, P, P, P, 4, 16, 16, None) == MIS
+
+
+def test_fp8_linear_argument_errors():
+    f = w8.lib().fp8_linear
+    need = w8.lib().fp8_linear_workspace_bytes(64, 32)
+    assert need == 64 * 32 + 256
+    assert f(P, P, P, P, -1, 16, 16, 1, P, 1 << 20, None) == SHAPE
+    assert f(P, P, P, P, 64, 16, 8, 1, P, 1 << 20, None) == UNSUP
+    # the FP8 path (fast_math, M > 8) needs the workspace; the default path does not read it
+    assert f(P, P, P, P, 64, 16, 32, 1, None, 0, None) == NULL
+    assert f(P, P, P, P, 64, 16, 32, 1, P + 4, need, None) == MIS
+    assert f(P, P, P, P, 64, 16, 32, 1, P, need - 1, None) == WS
+    import torch
+    if not torch.cuda.is_available():
+        assert f(P, P, P, P, 8, 16, 32, 1, None, 0, None) == DEV   # M <= 8: default maths, no workspace
+        assert f(P, P, P, P, 64, 16, 32, 0, None, 0, None) == DEV  # flag off: default maths
+        assert f(P, P, P, P, 64, 16, 32, 1, P, need, None) == DEV

@@ -35,6 +35,10 @@ _SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quantize_per_token": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "w8a8_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
+    "w8a16_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
+    "fp8_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "fp8_linear": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr,
+                                  ctypes.c_size_t, _c_ptr]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                  _c_ptr, ctypes.c_size_t, _c_ptr]),
@@ -159,6 +163,55 @@ def w8a8_gemm(a_q, a_scale, w_q, w_scale, out=None):
         raise ValueError("out must be [M, N]")
     _check("w8a8_gemm", lib().w8a8_gemm(a_q.data_ptr(), a_scale.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(),
                                         out.data_ptr(), M, N, K, _stream(a_q)))
+    return out
+
+
+def w8a16_gemm(x, w_q, w_scale, out=None):
+    """Default maths: y[m, n] = bf16(w_scale[n] * sum_k x[m, k] * dec(w_q[n, k])), x BF16 (not quantised)."""
+    import torch
+
+    _want(x, torch.bfloat16, 2, "x")
+    _want(w_q, torch.uint8, 2, "w_q")
+    _want(w_scale, torch.float32, 1, "w_scale")
+    M, K = x.shape
+    N, K2 = w_q.shape
+    if K2 != K or w_scale.shape[0] != N:
+        raise ValueError("shape mismatch between x, w_q and w_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _want(out, torch.bfloat16, 2, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check("w8a16_gemm", lib().w8a16_gemm(x.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(), out.data_ptr(), M, N, K,
+                                          _stream(x)))
+    return out
+
+
+def fp8_linear(x, w_q, w_scale, fast_math=True, out=None, workspace=None):
+    """The layer as the model page's runtime picks it: FP8 multiply (per-token
+    quantisation + w8a8_gemm) when ``fast_math`` and more than 8 tokens,
+    otherwise the default maths (w8a16_gemm)."""
+    import torch
+
+    _want(x, torch.bfloat16, 2, "x")
+    _want(w_q, torch.uint8, 2, "w_q")
+    _want(w_scale, torch.float32, 1, "w_scale")
+    M, K = x.shape
+    N, K2 = w_q.shape
+    if K2 != K or w_scale.shape[0] != N:
+        raise ValueError("shape mismatch between x, w_q and w_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _want(out, torch.bfloat16, 2, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    nbytes = int(lib().fp8_linear_workspace_bytes(M, K))
+    if workspace is None and fast_math and M > 8:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wlen = workspace.numel() if workspace is not None else 0
+    _check("fp8_linear", lib().fp8_linear(x.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(), out.data_ptr(), M, N, K,
+                                          1 if fast_math else 0, wptr, wlen, _stream(x)))
     return out
 
 

@@ -41,6 +41,22 @@ bool mul_ok(int64_t a, int64_t b) {  // a, b >= 0; a * b fits in int64
   return a == 0 || b <= INT64_MAX / a;
 }
 
+// Sizes accepted by the dense GEMM entry points.
+int check_dense_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N) || !mul_ok(M * N, 2) ||
+      !mul_ok(M * K, 2))
+    return W8A8_ERR_BAD_SHAPE;
+  if (K == 0 || K % 16 != 0 || K > (int64_t(1) << 20)) return W8A8_ERR_UNSUPPORTED;
+  if (N % 16 != 0 || N > (int64_t(1) << 20) || M > (int64_t(1) << 24)) return W8A8_ERR_UNSUPPORTED;
+  return W8A8_OK;
+}
+
+int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
+
+// The model page applies the FP8 multiply only to steps with more than 8
+// tokens at once; fewer always use the default maths.
+constexpr int64_t kFastMathMinTokens = 8;
+
 int launch_status(hipError_t e) {
   if (e == hipSuccess) return W8A8_OK;
   return W8A8_ERR_LAUNCH;
@@ -91,6 +107,46 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_gemm(a_q, a_scale, w_q, w_scale, y_bf16, M, N, K, stream));
+}
+
+int w8a16_gemm(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
+               int64_t N, int64_t K, hipStream_t stream) {
+  const int c = check_dense_shape(M, N, K);
+  if (c != W8A8_OK) return c;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!x_bf16 || !w_q || !w_scale || !y_bf16) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_bf16)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_w8a16_gemm(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
+}
+
+size_t fp8_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || !mul_ok(M, K)) return 0;
+  return (size_t)(align256(M * K) + align256(M * 4));
+}
+
+int fp8_linear(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
+               int64_t N, int64_t K, int fast_math, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int c = check_dense_shape(M, N, K);
+  if (c != W8A8_OK) return c;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!x_bf16 || !w_q || !w_scale || !y_bf16) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_bf16)) return W8A8_ERR_MISALIGNED;
+  const bool fp8_path = fast_math != 0 && M > kFastMathMinTokens;
+  if (fp8_path) {
+    if (!workspace) return W8A8_ERR_NULL_ARG;
+    if (!aligned16(workspace)) return W8A8_ERR_MISALIGNED;
+    if (workspace_bytes < fp8_linear_workspace_bytes(M, K)) return W8A8_ERR_WORKSPACE;
+  }
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  if (!fp8_path) return launch_status(w8a8::launch_w8a16_gemm(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(xq + align256(M * K));
+  const hipError_t e = w8a8::launch_quantize_rows(x_bf16, M, K, xq, xs, stream);
+  if (e != hipSuccess) return launch_status(e);
+  return launch_status(w8a8::launch_gemm(xq, xs, w_q, w_scale, y_bf16, M, N, K, stream));
 }
 
 }  // extern "C"
