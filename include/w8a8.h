@@ -283,14 +283,19 @@ size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int6
 /*
  * moe_w8a8_grouped — one routed-expert pass on buffers carved from
  * `workspace`, all in order 0: moe_route, moe_gate_up_swiglu_quant, then
- * moe_down_combine. out_bf16 [T, H]. I must be a multiple of 128. Running
- * the stack's two passes is two calls, the second on quantize_per_token of
- * the first call's output.
+ * moe_down_combine. out_bf16 [T, H]. I must be a multiple of 128.
+ *   out_q [T, H], out_scale [T]  optional (both NULL, or both set): also
+ *                 writes quantize_per_token(out_bf16), bit for bit, fused into
+ *                 the combine — the input of the next pass of the stack
+ *                 (sglang-metis 0.1.0, "How the model maps onto SGLang": every
+ *                 token passes through the stack twice on one set of weights).
+ * Running the two passes is two calls; the second takes the first call's
+ * out_q / out_scale as x_q / x_scale.
  */
 int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const float* topk_w,
                      const uint8_t* w13_q, const float* w13_scale, const uint8_t* w2_q, const float* w2_scale,
-                     uint16_t* out_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream);
+                     uint16_t* out_bf16, uint8_t* out_q, float* out_scale, int64_t T, int64_t H, int64_t I, int64_t E,
+                     int64_t topk, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -329,3 +329,26 @@ def test_mismatched_order_is_rejected(small):
     hs = torch.ones(small["T"] * small["k"], dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         w8.moe_down_combine(hq, hs, perm0, off0, to_dev(ids), to_dev(tw), dv["q2"], dv["s2"], order=1)
+
+
+@pytest.mark.parametrize("cfg", [dict(T=37, H=256, I=256, E=5, k=3), dict(T=301, H=272, I=384, E=9, k=4),
+                                 dict(T=64, H=2064, I=128, E=4, k=2), dict(T=16, H=8208, I=128, E=3, k=2)])
+def test_fused_output_quantisation(cfg):
+    """The pass's per-token FP8 output (made in the combine for H <= 8192, by
+    a separate quantisation beyond) equals quantize_per_token of its BF16
+    output bit for bit, and the oracle's quantiser on the same values."""
+    print(f"[fused out quant] {cfg}", flush=True)
+    d = quantized_moe(**cfg, n_outlier=2, seed=17)
+    dv = _dev(d)
+    ids, w = d["routes"][0]
+    args = (dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
+    plain = w8.moe_w8a8_grouped(*args)
+    out, q, s = w8.moe_w8a8_grouped(*args, quantize_output=True)
+    q2, s2 = w8.quantize_per_token(out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), bf16_bits(plain))
+    assert np.array_equal(q.cpu().numpy(), q2.cpu().numpy())
+    assert np.array_equal(s.cpu().numpy(), s2.cpu().numpy())
+    qo, so, _ = oracle.quantize_rows(oracle.bf16_bits_to_f64(bf16_bits(out)).astype(np.float32))
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(s.cpu().numpy(), so)

@@ -50,7 +50,7 @@ _SIGNATURES = {
     "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "w8a8_grouped_gemm": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
     "moe_w8a8_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 5),
-    "moe_w8a8_grouped": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
+    "moe_w8a8_grouped": (ctypes.c_int, [_c_ptr] * 11 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
 }
 
 
@@ -383,8 +383,13 @@ def moe_workspace(T: int, H: int, I: int, E: int, topk: int, device="cuda"):
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
-def moe_w8a8_grouped(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out=None, workspace=None):
-    """One routed-expert pass on per-token FP8 tokens: BF16 [T, H]."""
+def moe_w8a8_grouped(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out=None, workspace=None,
+                     quantize_output=False):
+    """One routed-expert pass on per-token FP8 tokens: BF16 [T, H].
+
+    With ``quantize_output`` the pass also returns the per-token FP8 version
+    of its output (codes [T, H], scales [T]), made in the combine: the input
+    of the next pass. Returns ``out`` or ``(out, out_q, out_scale)``."""
     import torch
 
     for t, dt, nd, n in ((x_q, torch.uint8, 2, "x_q"), (x_scale, torch.float32, 1, "x_scale"),
@@ -399,22 +404,35 @@ def moe_w8a8_grouped(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x_q.device)
     if workspace is None:
         workspace = moe_workspace(T, H, I, E, k, device=x_q.device)
+    oq = os_ = None
+    if quantize_output:
+        oq = torch.empty((T, H), dtype=torch.uint8, device=x_q.device)
+        os_ = torch.empty((T,), dtype=torch.float32, device=x_q.device)
     _check("moe_w8a8_grouped", lib().moe_w8a8_grouped(
         x_q.data_ptr(), x_scale.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w13_q.data_ptr(),
-        w13_scale.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), T, H, I, E, k,
+        w13_scale.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(),
+        oq.data_ptr() if quantize_output else None, os_.data_ptr() if quantize_output else None, T, H, I, E, k,
         workspace.data_ptr(), workspace.numel(), _stream(x_q)))
-    return out
+    return (out, oq, os_) if quantize_output else out
 
 
 def moe_ffn(x, routes, w13_q, w13_scale, w2_q, w2_scale, workspace=None):
     """The routed-expert stage run once per entry of ``routes`` with the same
-    weights, each pass fed the previous pass's BF16 output (every token goes
+    weights, each pass fed the previous pass's output (every token goes
     through the block stack two times on one set of weights; sglang-metis
-    0.1.0, "How the model maps onto SGLang"). ``routes`` is a list of (topk_ids, topk_w). Returns the
-    list of per-pass BF16 outputs."""
+    0.1.0, "How the model maps onto SGLang"). ``routes`` is a list of
+    (topk_ids, topk_w). The first pass's input is quantised per token here;
+    each later pass takes the per-token FP8 output that the previous pass's
+    combine wrote. Returns the list of per-pass BF16 outputs."""
     outs = []
-    for ids, w in routes:
-        xq, xs = quantize_per_token(x)
-        x = moe_w8a8_grouped(xq, xs, ids, w, w13_q, w13_scale, w2_q, w2_scale, workspace=workspace)
-        outs.append(x)
+    xq, xs = quantize_per_token(x)
+    for i, (ids, w) in enumerate(routes):
+        last = i + 1 == len(routes)
+        r = moe_w8a8_grouped(xq, xs, ids, w, w13_q, w13_scale, w2_q, w2_scale, workspace=workspace,
+                             quantize_output=not last)
+        if last:
+            outs.append(r)
+        else:
+            out, xq, xs = r
+            outs.append(out)
     return outs

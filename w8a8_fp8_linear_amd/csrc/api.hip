@@ -267,7 +267,7 @@ int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* pe
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
-                                                 out_bf16, y_f32, T, H, I, E, topk, order, stream));
+                                                 out_bf16, y_f32, nullptr, nullptr, T, H, I, E, topk, order, stream));
 }
 
 size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -299,8 +299,8 @@ size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int6
 
 int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* topk_ids, const float* topk_w,
                      const uint8_t* w13_q, const float* w13_scale, const uint8_t* w2_q, const float* w2_scale,
-                     uint16_t* out_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+                     uint16_t* out_bf16, uint8_t* out_q, float* out_scale, int64_t T, int64_t H, int64_t I, int64_t E,
+                     int64_t topk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
   if (I % kFusedIMultiple != 0) return W8A8_ERR_UNSUPPORTED;
@@ -308,13 +308,15 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
   if (T == 0) return W8A8_OK;
   if (any_null({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
     return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
+  if ((out_q == nullptr) != (out_scale == nullptr)) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, out_q, out_scale,
+                    workspace}))
     return W8A8_ERR_MISALIGNED;
   if (workspace_bytes < w8a8::moe_workspace_bytes(T, H, I, E, topk)) return W8A8_ERR_WORKSPACE;
   const int d = check_device();
   if (d != W8A8_OK) return d;
-  return launch_status(w8a8::launch_moe(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, T,
-                                        H, I, E, topk, workspace, stream));
+  return launch_status(w8a8::launch_moe(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16,
+                                        out_q, out_scale, T, H, I, E, topk, workspace, stream));
 }
 
 }  // extern "C"

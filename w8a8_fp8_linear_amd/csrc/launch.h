@@ -51,11 +51,12 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
 
 // y: [T*topk, H] float32 scratch (down_combine_scratch_bytes).
 size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk);
+// out_q / out_s (both NULL or both set): also quantize_per_token(out).
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
                                const int32_t* offsets, const int32_t* ids, const float* tw,
-                               const uint8_t* w2, const float* s2, uint16_t* out, float* y, int64_t T,
-                               int64_t H, int64_t I, int64_t E, int64_t topk, int order,
-                               hipStream_t stream);
+                               const uint8_t* w2, const float* s2, uint16_t* out, float* y,
+                               uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I,
+                               int64_t E, int64_t topk, int order, hipStream_t stream);
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids,
                                   const uint8_t* w13, const float* s13, uint16_t* gu, int32_t* perm,
@@ -64,7 +65,7 @@ hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int3
 
 hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, const float* tw,
                       const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
-                      uint16_t* out, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
-                      void* ws, hipStream_t stream);
+                      uint16_t* out, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I,
+                      int64_t E, int64_t topk, void* ws, hipStream_t stream);
 
 }  // namespace w8a8

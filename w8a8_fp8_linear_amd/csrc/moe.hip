@@ -40,7 +40,9 @@
 //  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots, added
 //    in the fixed order j = 0, 1, ... (deterministic, no atomics; float32
 //    atomics measured ~3x slower than this whole stage). The k rows of a
-//    token are contiguous, so this is one streaming pass.
+//    token are contiguous, so this is one streaming pass. combine_quant also
+//    quantises each output row per token (the next pass's input) in the
+//    same pass.
 #include <algorithm>
 
 #include "device.h"
@@ -553,19 +555,16 @@ __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, i
   if (i < n) p[i] = 0u;
 }
 
-// out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots,
-// added in the order j = 0, 1, ... in float32 (deterministic). One thread
-// per 8 columns; the k rows of a token are contiguous in y.
-__global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                                                     int64_t T, int topk, int Eids, int H,
-                                                     uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = H >> 3;
-  const int64_t t = i / per_row;
-  if (t >= T) return;
-  const int c0 = (int)(i - t * per_row) << 3;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  constexpr int kBatch = 8;  // rows loaded before any is added (a dropped slot's row is read but not used)
+// Sum of a token's valid slot rows at columns c0 .. c0 + 7, in the order
+// j = 0, 1, ... in float32 (deterministic). The k rows of a token are
+// contiguous in y; they are loaded (non-temporal: each byte is read once;
+// measured 8% faster on this stage) before any is added, and a dropped
+// slot's row is read but not used.
+__device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __restrict__ ids, int64_t t, int topk,
+                                  int Eids, int H, int c0, float4& a, float4& b) {
+  a = make_float4(0.f, 0.f, 0.f, 0.f);
+  b = a;
+  constexpr int kBatch = 8;
   for (int j0 = 0; j0 < topk; j0 += kBatch) {
     float4 u[kBatch], v[kBatch];
     bool ok[kBatch];
@@ -575,9 +574,10 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
       const int64_t slot = t * topk + (j < topk ? j : 0);
       const int id = ids[slot];
       ok[jj] = j < topk && id >= 0 && id < Eids;
-      const float4* src = reinterpret_cast<const float4*>(y + slot * H + c0);
-      u[jj] = src[0];
-      v[jj] = src[1];
+      const v4f* src = reinterpret_cast<const v4f*>(y + slot * H + c0);
+      const v4f t0 = __builtin_nontemporal_load(src), t1 = __builtin_nontemporal_load(src + 1);
+      u[jj] = make_float4(t0[0], t0[1], t0[2], t0[3]);
+      v[jj] = make_float4(t1[0], t1[1], t1[2], t1[3]);
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
@@ -586,12 +586,67 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
       b.x += v[jj].x; b.y += v[jj].y; b.z += v[jj].z; b.w += v[jj].w;
     }
   }
-  uint4 o;
-  o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
-  o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
-  o.z = f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16);
-  o.w = f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16);
-  *reinterpret_cast<uint4*>(out + t * H + c0) = o;
+}
+
+__device__ inline uint4 to_bf16x8(float4 a, float4 b) {
+  return make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16), f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
+                    f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16), f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
+}
+
+// out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots.
+// One thread per 8 columns.
+__global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y, const int32_t* __restrict__ ids,
+                                                     int64_t T, int topk, int Eids, int H,
+                                                     uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = H >> 3;
+  const int64_t t = i / per_row;
+  if (t >= T) return;
+  const int c0 = (int)(i - t * per_row) << 3;
+  float4 a, b;
+  sum_slots8(y, ids, t, topk, Eids, H, c0, a, b);
+  *reinterpret_cast<uint4*>(out + t * H + c0) = to_bf16x8(a, b);
+}
+
+// The combine with the next pass's per-token quantisation fused in: one
+// workgroup per token, PER chunks of 8 columns per thread (H <= 2048 * PER).
+// Writes out[t] (BF16) and q[t] / qs[t], exactly what quantize_per_token
+// makes of out[t]: amax on the BF16 bits, s = fl32(amax / 448), codes of
+// fl32(x / s) (the same shared quantiser code).
+template <int PER>
+__global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y, const int32_t* __restrict__ ids,
+                                                     int topk, int Eids, int H, uint16_t* __restrict__ out,
+                                                     uint8_t* __restrict__ q, float* __restrict__ qs) {
+  __shared__ uint32_t wmax[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint4 vb[PER];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int c0 = (tid + 256 * p) << 3;
+    vb[p] = make_uint4(0u, 0u, 0u, 0u);
+    if (c0 < H) {
+      float4 a, b;
+      sum_slots8(y, ids, t, topk, Eids, H, c0, a, b);
+      vb[p] = to_bf16x8(a, b);
+      *reinterpret_cast<uint4*>(out + t * H + c0) = vb[p];
+      const uint32_t m = absmax8(vb[p]);
+      amax = amax > m ? amax : m;
+    }
+  }
+  amax = wave_max_u32(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s = row_scale(amax);
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int c0 = (tid + 256 * p) << 3;
+    if (c0 < H) *reinterpret_cast<uint2*>(q + t * H + c0) = quant8(vb[p], s, r);
+  }
+  if (tid == 0) qs[t] = s;
 }
 
 int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
@@ -700,8 +755,8 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
 // to its own row of y), then the per-token combine.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm, const int32_t* offsets,
                                const int32_t* ids, const float* tw, const uint8_t* w2, const float* s2, uint16_t* out,
-                               float* y, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
-                               hipStream_t stream) {
+                               float* y, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I, int64_t E,
+                               int64_t topk, int order, hipStream_t stream) {
   GroupedArgs a{};
   a.A = qh;
   a.sA = sh;
@@ -719,10 +774,23 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   a.K = (int)I;
   const hipError_t err = run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, kDownY, kDnOcc>(a, T * topk, stream);
   if (err != hipSuccess) return err;
+  if (out_q != nullptr && H <= 2048 * 4) {
+    const dim3 grid((unsigned)T);
+    if (H <= 2048)
+      hipLaunchKernelGGL(combine_quant<1>, grid, dim3(256), 0, stream, y, ids, (int)topk, (int)E, (int)H, out, out_q, out_s);
+    else if (H <= 4096)
+      hipLaunchKernelGGL(combine_quant<2>, grid, dim3(256), 0, stream, y, ids, (int)topk, (int)E, (int)H, out, out_q, out_s);
+    else
+      hipLaunchKernelGGL(combine_quant<4>, grid, dim3(256), 0, stream, y, ids, (int)topk, (int)E, (int)H, out, out_q, out_s);
+    return hipGetLastError();
+  }
   const int64_t threads = T * (H / 8);
   hipLaunchKernelGGL(combine_slots, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, y, ids, T,
                      (int)topk, (int)E, (int)H, out);
-  return hipGetLastError();
+  if (out_q == nullptr) return hipGetLastError();
+  const hipError_t cerr = hipGetLastError();  // rows longer than the fused kernel holds: quantise separately
+  if (cerr != hipSuccess) return cerr;
+  return launch_quantize_rows(out, T, H, out_q, out_s, stream);
 }
 
 size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk) { return (size_t)(T * topk * H * 4); }
@@ -758,8 +826,9 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t t
 // One pass, all on the expert-major order: route, gate/up + SwiGLU +
 // requantisation, down projection into per-slot rows, combine.
 hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, const float* tw, const uint8_t* w13,
-                      const float* s13, const uint8_t* w2, const float* s2, uint16_t* out, int64_t T, int64_t H,
-                      int64_t I, int64_t E, int64_t topk, void* ws, hipStream_t stream) {
+                      const float* s13, const uint8_t* w2, const float* s2, uint16_t* out, uint8_t* out_q,
+                      float* out_s, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, void* ws,
+                      hipStream_t stream) {
   const MoeLayout L = moe_layout(T, H, I, E, topk);
   uint8_t* b = static_cast<uint8_t*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
@@ -772,8 +841,8 @@ hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, co
   err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, T, H, I, E, topk, 0,
                                     b + L.amax, stream);
   if (err != hipSuccess) return err;
-  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<float*>(b + L.big), T, H,
-                             I, E, topk, 0, stream);
+  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<float*>(b + L.big), out_q,
+                             out_s, T, H, I, E, topk, 0, stream);
 }
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids, const uint8_t* w13,

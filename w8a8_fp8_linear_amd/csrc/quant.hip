@@ -27,49 +27,6 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row, 256 threads
 
-__device__ inline uint32_t absmax8(uint4 v) {
-  uint32_t m = 0;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
-    m = m > lo ? m : lo;
-    m = m > hi ? m : hi;
-  }
-  return m;
-}
-
-// 8 BF16 values -> 8 E4M3 codes of fl32(x / s) (little-endian, element 0 in
-// byte 0); r = fl32(1 / s), or a non-finite r (a subnormal scale) to divide
-// every value.
-__device__ inline uint2 quant8(uint4 v, float s, float r) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float x[8], q[8];
-  bool near = !(r < 3.0e38f);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_lo(w[i]);
-    x[2 * i + 1] = bf16_hi(w[i]);
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    q[k] = x[k] * r;
-    near |= e4m3_boundary_near(q[k]);
-  }
-  if (__builtin_expect(near, 0)) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) q[k] = x[k] / s;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) q[k] = clamp448(q[k]);
-  return make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
-}
-
-__device__ inline float row_scale(uint32_t amax_bits) {
-  if (amax_bits == 0) return 1.0f;
-  return __uint_as_float(amax_bits << 16) / 448.0f;
-}
-
 template <int NCH>
 __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t M,
                                                         int64_t K, uint8_t* __restrict__ q,
