@@ -51,7 +51,7 @@
 namespace w8a8 {
 namespace {
 
-constexpr int kRouteChunk = 4096;       // slots per routing block (4 waves x 1024)
+constexpr int kRouteChunk = 1024;       // slots per routing block (4 waves x 256)
 constexpr int kRouteSub = kRouteChunk / 4;
 
 __device__ inline int bits_for(int v) {  // bits needed to tell 0..v apart
