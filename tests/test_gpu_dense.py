@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import bf16_bits, gemm_report, record, to_dev, to_dev_bf16
+from gpu_util import bf16_bits, gemm_report, record, to_dev, to_dev_bf16, w8a16_report
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +240,53 @@ def test_gemm_accumulation_model():
                                    if ks not in same_group], "exact": 2.0 ** -6}
     print("accumulation model", rep, flush=True)
     record("E4M3 MFMA 8-group alignment", rep)
+
+
+# ---- the largest sizes the entry points accept (32-bit offsets inside the kernels)
+
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_gemm_max_k(M):
+    """K = 2**20, the largest accepted: the skinny (M = 16) and tiled (M = 64) kernels."""
+    K, N = 1 << 20, 32
+    print(f"[gemm max K] M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M)
+    x = synth.activations(rng, M, K, n_outlier=0)
+    w = synth.weights(rng, (N, K))
+    qx, sx, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(x))
+    qw, sw, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(w))
+    got = _run_gemm(qx, sx, qw, sw)
+    rep = gemm_report(got, qx, sx, qw, sw)
+    record(f"gemm max K {M}x{N}x{K}", rep)
+    assert rep["n_bound_violations"] == 0, rep
+    assert rep["frobenius"] <= 4e-3, rep
+    y16 = bf16_bits(w8.w8a16_gemm(to_dev_bf16(x), to_dev(qw), to_dev(sw)))
+    torch.cuda.synchronize()
+    rep16 = w8a16_report(y16, x, qw, sw)
+    record(f"w8a16 max K {M}x{N}x{K}", rep16)
+    assert rep16["n_bound_violations"] == 0, rep16
+
+
+def test_gemm_max_n():
+    """N = 2**20 output channels (the largest accepted), one token, K = 64."""
+    M, N, K = 1, 1 << 20, 64
+    print(f"[gemm max N] {M}x{N}x{K}", flush=True)
+    rng = np.random.default_rng(5)
+    x = synth.activations(rng, M, K, n_outlier=0)
+    qw = rng.integers(0, 256, size=(N, K), dtype=np.int64).astype(np.uint8)
+    qw[(qw & 0x7F) == 0x7F] = 0x7E
+    sw = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    qx, sx, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(x))
+    got = _run_gemm(qx, sx, qw, sw)
+    rep = gemm_report(got, qx, sx, qw, sw)
+    record(f"gemm max N {M}x{N}x{K}", rep)
+    assert rep["n_bound_violations"] == 0, rep
+
+
+def test_quantize_many_rows():
+    """4M rows of 16 values (67 MB of BF16): row indexing past 2**22 rows."""
+    M, K = 1 << 22, 16
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((M, K), dtype=np.float32) * np.float32(3)).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation is fine: any BF16 pattern is an input
+    _quant_check(bits, f"many rows {M}x{K}")

@@ -80,7 +80,7 @@ def oracle_route(ids, E, order):
 
 @pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (37, 3, 5), (1000, 8, 7), (4096, 8, 64), (16384, 8, 64),
-                                   (513, 4, 130), (2000, 2, 1024)])
+                                   (513, 4, 130), (2000, 2, 1024), (300, 64, 16)])
 def test_route_bitexact(T, k, E, order):
     if order == 1 and k * E > 1024:
         pytest.skip("more than 1024 routing groups")
