@@ -375,6 +375,36 @@ def bench_moe_two_pass(reps=5, warmup=2):
             "tokens_per_s": T / (ms * 1e-3), "stage_us_one_pass": stages}
 
 
+def bench_moe_pages_shapes(reps=10, warmup=3):
+    """The two-pass routed-expert FFN at the model pages' expert shapes."""
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    out = {}
+    for cfg in (synth.MOE_PRAXIS, synth.MOE_LOGOS):
+        T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+        x, q13, s13, q2, s2, routes = _moe_inputs(cfg)
+        ws = w8.moe_workspace(T, H, I, E, k)
+        for _ in range(warmup):
+            w8.moe_ffn(x, routes, q13, s13, q2, s2, workspace=ws)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        evs = _events(reps)
+        for a, b in evs:
+            a.record(stream)
+            w8.moe_ffn(x, routes, q13, s13, q2, s2, workspace=ws)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = _avg_ms(evs)
+        flops = 2 * (2.0 * T * k * 2 * I * H + 2.0 * T * k * H * I)
+        out[cfg["name"]] = {"us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                            "frac_fp8_peak": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+                            "tokens_per_s": T / (ms * 1e-3)}
+    return out
+
+
 def cpu_baseline():
     """The CPU oracle on the full prefill workload (activation quantisation,
     exact float64 GEMM, BF16 rounding), timed once on this host."""
@@ -436,12 +466,14 @@ def main():
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         dec = bench_decode()
-    moe_gu = moe_ffn = None
+    moe_gu = moe_ffn = moe_pages = None
     if not args.no_moe:
         print("[bench] routed gate/up", file=sys.stderr, flush=True)
         moe_gu = bench_moe_gate_up()
         print("[bench] routed FFN, two passes", file=sys.stderr, flush=True)
         moe_ffn = bench_moe_two_pass()
+        print("[bench] routed FFN at the pages' expert shapes", file=sys.stderr, flush=True)
+        moe_pages = bench_moe_pages_shapes()
     dm = None
     if not args.no_default_maths:
         print("[bench] default maths (W8A16)", file=sys.stderr, flush=True)
@@ -480,6 +512,7 @@ def main():
         "decode": dec,
         "moe_gate_up": moe_gu,
         "moe_two_pass": moe_ffn,
+        "moe_pages_shapes": moe_pages,
         "default_maths": dm,
         "cpu_baseline": cpu,
     }

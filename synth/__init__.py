@@ -105,6 +105,13 @@ MOE_GATE_UP = dict(name="moe_gate_up_T4096_H2048_I512_E64_k8", T=4096, H=2048, I
                    n_outlier=20, passes=1)
 MOE_TWO_PASS = dict(name="moe_ffn_2pass_T16384_H2048_I512_E64_k8", T=16384, H=2048, I=512, E=64,
                     k=8, n_outlier=20, passes=2)
+# The model pages' own expert shapes: 128 (Praxis) or 192 (Logos) routed experts
+# in a 1,024-wide latent space, four per token ("Architecture" sections). The
+# expert intermediate width is not on the pages: 512 here, a parameter.
+MOE_PRAXIS = dict(name="moe_ffn_2pass_T4096_H1024_I512_E128_k4", T=4096, H=1024, I=512, E=128, k=4,
+                  n_outlier=10, passes=2)
+MOE_LOGOS = dict(name="moe_ffn_2pass_T4096_H1024_I512_E192_k4", T=4096, H=1024, I=512, E=192, k=4,
+                 n_outlier=10, passes=2)
 
 
 def dense_workload(M: int, K: int, N: int, n_outlier: int = 0, seed: int = 0, **_):

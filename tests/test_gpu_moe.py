@@ -352,3 +352,21 @@ def test_fused_output_quantisation(cfg):
     qo, so, _ = oracle.quantize_rows(oracle.bf16_bits_to_f64(bf16_bits(out)).astype(np.float32))
     assert np.array_equal(q.cpu().numpy(), qo)
     assert np.array_equal(s.cpu().numpy(), so)
+
+
+@pytest.mark.parametrize("E", [128, 192])
+def test_pages_expert_shapes(E):
+    """The model pages' expert shapes (128 or 192 experts, latent width 1024,
+    top-4; the intermediate width 512 is a reading): a full pass against the
+    oracle on every token, 512 tokens."""
+    print(f"[pages shape] E={E}", flush=True)
+    d = quantized_moe(T=512, H=1024, I=512, E=E, k=4, n_outlier=5, seed=E)
+    dv = _dev(d)
+    ids, w = d["routes"][0]
+    out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    ref64 = _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, np.arange(d["T"]))
+    rep = bf16_compare(bf16_bits(out), ref64)
+    print(f"pages shape E={E}", rep, flush=True)
+    record(f"moe full pass pages shape T=512 H=1024 I=512 E={E} k=4", rep)
+    assert rep["frobenius"] <= 4e-3, rep

@@ -660,6 +660,11 @@ int route_chunks(int64_t n) { return (int)((n + kRouteChunk - 1) / kRouteChunk);
 // for the gate/up: this shape was the fastest or within noise for both.
 constexpr int kGuBM = 256, kGuBN = 256, kGuWGM = 2, kGuWGN = 4, kGuOcc = 2;
 constexpr int kDnBM = 256, kDnBN = 256, kDnWGM = 2, kDnWGN = 4, kDnOcc = 2;
+// Groups of fewer than kSmallGroupRows rows on average (few tokens per
+// expert, e.g. 128 experts at top-4) use 128-row tiles: with 256-row tiles
+// most of each tile would be padding.
+constexpr int64_t kSmallGroupRows = 512;
+
 
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
@@ -670,6 +675,14 @@ hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
   hipLaunchKernelGGL((grouped_tiled<BM, BN, WGM, WGN, MODE, OCC>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+// One grouped launch in the tile shape that suits the average group size.
+template <int MODE>
+hipError_t run_grouped_auto(const GroupedArgs& a, int64_t max_rows, int64_t avg_rows, hipStream_t stream) {
+  if (avg_rows < kSmallGroupRows) return run_grouped<128, 256, 2, 4, MODE, 2>(a, max_rows, stream);
+  if (MODE == kDownY) return run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, MODE, kDnOcc>(a, max_rows, stream);
+  return run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, MODE, kGuOcc>(a, max_rows, stream);
 }
 
 GroupedArgs gate_up_args(const uint8_t* xq, const float* xs, const int32_t* perm, const int32_t* offsets, int G,
@@ -720,7 +733,7 @@ hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const
                                        hipStream_t stream) {
   GroupedArgs a = gate_up_args(xq, xs, perm, offsets, (int)route_groups(topk, E, order), w13, s13, T, H, I, E, topk);
   a.out_bf16 = gu;
-  return run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, kGateUp, kGuOcc>(a, T * topk, stream);
+  return run_grouped_auto<kGateUp>(a, T * topk, T * topk / a.G, stream);
 }
 
 size_t gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk) {
@@ -743,7 +756,7 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
   a.out_f32 = h;
   a.row_amax = amax;
   a.dst_row = dst_row;
-  hipError_t err = run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, kGateUpH, kGuOcc>(a, n, stream);
+  hipError_t err = run_grouped_auto<kGateUpH>(a, n, n / G, stream);
   if (err != hipSuccess) return err;
   const int64_t threads = n * (I / 16);
   hipLaunchKernelGGL(requant_rows, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, h, amax,
@@ -772,7 +785,7 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   a.out_f32 = y;
   a.N = (int)H;
   a.K = (int)I;
-  const hipError_t err = run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, kDownY, kDnOcc>(a, T * topk, stream);
+  const hipError_t err = run_grouped_auto<kDownY>(a, T * topk, T * topk / a.G, stream);
   if (err != hipSuccess) return err;
   if (out_q != nullptr && H <= 2048 * 4) {
     const dim3 grid((unsigned)T);
