@@ -22,6 +22,11 @@ What it defines, and where the pages state it:
   flag the FP8 weights are widened to 16 bits and the product is taken in
   BF16 on unquantised activations (Lernex/Metis-1.6-Logos-FP8, "What
   --fast-math does").
+* MXFP4 (``mxfp4``): the 4-bit E2M1 expert format with one power-of-two
+  scale per 32 inputs, the GPU-native analogue of the NVFP4 experts
+  (Lernex/Metis-1.6-Praxis-NVFP4, "What is in NVFP4": E2M1 values with a
+  scale per small block; "What --fast-math does": expert inputs rounded to
+  FP4), its block quantiser, linear layer and routed-expert pass.
 * The routed-expert chain (``moe``): routed experts in FP8 with the same
   scheme, top-k routing, the stack run twice with shared weights
   (Lernex/Metis-1.6-Praxis, "Architecture"; sglang-metis 0.1.0, "How the
@@ -38,10 +43,13 @@ from .bf16 import bf16_bits_to_f64, round_to_bf16_bits
 from .quant import bf16_bits_to_f32, quantize_rows
 from .linear import w8a8_linear, w8a8_linear_int, w8a16_linear
 from .moe import (route, grouped_gate_up, moe_pass, moe_two_pass, swiglu_f32)
+from .mxfp4 import (e2m1_decode, e2m1_encode, e8m0_value, mx_dequant, mx_quantize_rows, mx_unpack, mxfp4_linear,
+                    moe_mxfp4_pass, moe_mxfp4_two_pass)
 
 __all__ = [
     "E4M3_MAX", "decode", "decode_table", "encode", "encode_bits", "finite_codes", "magnitudes",
     "bf16_bits_to_f64", "round_to_bf16_bits", "bf16_bits_to_f32", "quantize_rows",
     "w8a8_linear", "w8a8_linear_int", "w8a16_linear", "route", "grouped_gate_up", "moe_pass", "moe_two_pass",
-    "swiglu_f32",
+    "swiglu_f32", "e2m1_decode", "e2m1_encode", "e8m0_value", "mx_dequant", "mx_quantize_rows", "mx_unpack",
+    "mxfp4_linear", "moe_mxfp4_pass", "moe_mxfp4_two_pass",
 ]
