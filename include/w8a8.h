@@ -297,6 +297,103 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
                      uint16_t* out_bf16, uint8_t* out_q, float* out_scale, int64_t T, int64_t H, int64_t I, int64_t E,
                      int64_t topk, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * MXFP4 routed experts
+ *
+ * The 4-bit model page keeps the routed experts in a 4-bit format (E2M1
+ * values with a scale per small block of inputs) and under fast-math rounds
+ * each expert input to FP4 as well (Lernex/Metis-1.6-Praxis-NVFP4, "What is
+ * in NVFP4" and "What --fast-math does"). Its blocks are 16 inputs with an
+ * E4M3 scale; these calls use the block format that gfx950's scaled matrix
+ * cores take natively, OCP MXFP4: blocks of 32 consecutive inputs along K,
+ * one E8M0 (power-of-two) scale each.
+ *
+ * Formats
+ *   E2M1   4-bit codes, two per byte: element 2i of a row in the low nibble of
+ *          byte i. Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign.
+ *   E8M0   one byte per block, value 2^(e - 127) (0xFF is NaN, never written).
+ *   A row of K values is K/2 code bytes and K/32 scale bytes; matrices are
+ *   row-major: codes [rows, K/2], scales [rows, K/32].
+ * Quantisation of a block (OCP MX v1.0): X = floor(log2(max |x|)) - 2,
+ * clamped to [-127, 127] (an all-zero block gets X = 0); each element is
+ * x / 2^X (exact) rounded to nearest, ties to even, magnitudes above 6
+ * saturating to 6, a negative value that rounds to zero giving 0x8.
+ *
+ * The expert chain is that of the FP8 calls above with every expert input
+ * and weight in MXFP4: tokens are quantised once over H, h = silu(g) * u
+ * (float32) is quantised per routed copy over I, y = topk_w * product, and
+ * the k outputs of a token are summed in float32 in the order j = 0, 1, ...
+ * and rounded once to BF16.
+ * Shapes: x_q [T, H/2] / x_scale [T, H/32]; w13_q [E, 2I, H/2] /
+ * w13_scale [E, 2I, H/32] (rows 0..I-1 gate, I..2I-1 up); w2_q [E, H, I/2] /
+ * w2_scale [E, H, I/32]; h_q [T*topk, I/2] / h_scale [T*topk, I/32].
+ * Limits: as the FP8 expert calls, and H and I positive multiples of 128.
+ * Scales are applied inside the matrix-core product; products of two E2M1
+ * values are exact, sums are float32.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * mxfp4_quantize — BF16 rows -> MXFP4 codes and E8M0 block scales, by the
+ * rule above. Bit-exact and deterministic.
+ *   x_bf16 [M, K]; q_fp4 [M, K/2]; scale_e8m0 [M, K/32]
+ *   K a positive multiple of 32, K <= 2^24.
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, DEVICE, LAUNCH.
+ */
+int mxfp4_quantize(const uint16_t* x_bf16, int64_t M, int64_t K, uint8_t* q_fp4, uint8_t* scale_e8m0,
+                   hipStream_t stream);
+
+/*
+ * moe_mxfp4_gate_up_bf16 — grouped gate/up projection on MXFP4 operands,
+ * BF16 result: gu_bf16[r, :] = bf16( x[t] . W13[e]^T ) for the r-th sorted
+ * slot (t = perm[r] / topk, e its expert), gu_bf16 [T*topk, 2I]; rows from
+ * offsets[G] on are left untouched. perm/offsets from moe_route in `order`.
+ */
+int moe_mxfp4_gate_up_bf16(const uint8_t* x_q, const uint8_t* x_scale, const int32_t* perm, const int32_t* offsets,
+                           const uint8_t* w13_q, const uint8_t* w13_scale, uint16_t* gu_bf16, int64_t T, int64_t H,
+                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+/*
+ * moe_mxfp4_gate_up_swiglu_quant — the gate/up projection with the expert
+ * activation and the MXFP4 quantisation of h fused in: h = silu(g) * u in
+ * float32 from the slot's gate/up row, then h_q / h_scale of h by the block
+ * rule. The row a slot's h goes to is its sorted row under perm, or
+ * dst_row[slot] when dst_row is given (as for moe_gate_up_swiglu_quant).
+ * No workspace: an MX block's scale needs only its own 32 values.
+ */
+int moe_mxfp4_gate_up_swiglu_quant(const uint8_t* x_q, const uint8_t* x_scale, const int32_t* perm,
+                                   const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13_q,
+                                   const uint8_t* w13_scale, uint8_t* h_q, uint8_t* h_scale, int64_t T, int64_t H,
+                                   int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+/*
+ * moe_mxfp4_down_combine — grouped down projection and combine:
+ *   y[slot, :]  = topk_w[slot] * (h[r] . W2[e]^T)   (float32, sorted row r)
+ *   out_bf16[t] = bf16( sum over valid j, in order j = 0, 1, ... of y[t*topk + j] )
+ *   y_f32 [T*topk, H] is caller-provided float32 scratch.
+ *   out_q [T, H/2], out_scale [T, H/32]  optional (both NULL or both set):
+ *               mxfp4_quantize(out_bf16), bit for bit, fused into the
+ *               combine — the next pass's expert input.
+ */
+int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int32_t* perm, const int32_t* offsets,
+                           const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const uint8_t* w2_scale,
+                           uint16_t* out_bf16, float* y_f32, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
+                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+/* Bytes of scratch moe_mxfp4_grouped needs (0 for invalid sizes). */
+size_t moe_mxfp4_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+
+/*
+ * moe_mxfp4_grouped — one MXFP4 routed-expert pass on buffers carved from
+ * `workspace`, all in order 0: moe_route, moe_mxfp4_gate_up_swiglu_quant,
+ * moe_mxfp4_down_combine. out_bf16 [T, H]; out_q / out_scale as for
+ * moe_mxfp4_down_combine. The second pass of the stack is a second call on
+ * the first call's out_q / out_scale.
+ */
+int moe_mxfp4_grouped(const uint8_t* x_q, const uint8_t* x_scale, const int32_t* topk_ids, const float* topk_w,
+                      const uint8_t* w13_q, const uint8_t* w13_scale, const uint8_t* w2_q, const uint8_t* w2_scale,
+                      uint16_t* out_bf16, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H, int64_t I,
+                      int64_t E, int64_t topk, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

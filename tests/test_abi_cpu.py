@@ -109,3 +109,41 @@ def test_fp8_linear_argument_errors():
         assert f(P, P, P, P, 8, 16, 32, 1, None, 0, None) == DEV   # M <= 8: default maths, no workspace
         assert f(P, P, P, P, 64, 16, 32, 0, None, 0, None) == DEV  # flag off: default maths
         assert f(P, P, P, P, 64, 16, 32, 1, P, need, None) == DEV
+
+
+def test_mxfp4_quantize_argument_errors():
+    f = w8.lib().mxfp4_quantize
+    assert f(P, -1, 32, P, P, None) == SHAPE
+    assert f(P, 4, 16, P, P, None) == UNSUP      # K must be a multiple of 32
+    assert f(P, 4, 0, P, P, None) == UNSUP
+    assert f(P, 0, 32, P, P, None) == OK
+    assert f(None, 4, 32, P, P, None) == NULL
+    assert f(P, 4, 32, P, None, None) == NULL
+    assert f(P, 4, 32, P, P + 8, None) == MIS
+    import torch
+    if not torch.cuda.is_available():
+        assert f(P, 4, 32, P, P, None) == DEV
+
+
+def test_mxfp4_expert_argument_errors():
+    L = w8.lib()
+    T, H, I, E, k = 64, 256, 128, 8, 2
+    # H and I must be multiples of 128
+    assert L.moe_mxfp4_gate_up_bf16(P, P, P, P, P, P, P, T, 192, I, E, k, 0, None) == UNSUP
+    assert L.moe_mxfp4_gate_up_swiglu_quant(P, P, P, P, None, P, P, P, P, T, H, 64, E, k, 0, None) == UNSUP
+    assert L.moe_mxfp4_gate_up_swiglu_quant(P, P, P, P, None, P, P, P, P, T, H, I, E, k, 2, None) == UNSUP
+    assert L.moe_mxfp4_down_combine(*([P] * 12), -1, H, I, E, k, 0, None) == SHAPE
+    assert L.moe_mxfp4_down_combine(*([P] * 12), 0, H, I, E, k, 0, None) == OK
+    # out_q and out_scale come together
+    assert L.moe_mxfp4_down_combine(*([P] * 10), P, None, T, H, I, E, k, 0, None) == NULL
+    assert L.moe_mxfp4_gate_up_bf16(P, None, P, P, P, P, P, T, H, I, E, k, 0, None) == NULL
+    assert L.moe_mxfp4_gate_up_swiglu_quant(P, P, P, P, P + 4, P, P, P, P, T, H, I, E, k, 0, None) == MIS
+    need = L.moe_mxfp4_workspace_bytes(T, H, I, E, k)
+    assert need > T * k * H * 4 and L.moe_mxfp4_workspace_bytes(T, H, 96, E, k) == 0
+    g = L.moe_mxfp4_grouped
+    assert g(*([P] * 9), None, None, T, H, I, E, k, P, need - 1, None) == WS
+    assert g(*([P] * 9), P, None, T, H, I, E, k, P, need, None) == NULL
+    assert g(*([P] * 9), None, None, T, H, I, 0, k, P, need, None) == UNSUP
+    import torch
+    if not torch.cuda.is_available():
+        assert g(*([P] * 9), None, None, T, H, I, E, k, P, need, None) == DEV

@@ -51,6 +51,12 @@ _SIGNATURES = {
     "w8a8_grouped_gemm": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
     "moe_w8a8_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 5),
     "moe_w8a8_grouped": (ctypes.c_int, [_c_ptr] * 11 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
+    "mxfp4_quantize": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "moe_mxfp4_gate_up_bf16": (ctypes.c_int, [_c_ptr] * 7 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
+    "moe_mxfp4_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
+    "moe_mxfp4_down_combine": (ctypes.c_int, [_c_ptr] * 12 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
+    "moe_mxfp4_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 5),
+    "moe_mxfp4_grouped": (ctypes.c_int, [_c_ptr] * 11 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
 }
 
 
@@ -430,6 +436,171 @@ def moe_ffn(x, routes, w13_q, w13_scale, w2_q, w2_scale, workspace=None):
         last = i + 1 == len(routes)
         r = moe_w8a8_grouped(xq, xs, ids, w, w13_q, w13_scale, w2_q, w2_scale, workspace=workspace,
                              quantize_output=not last)
+        if last:
+            outs.append(r)
+        else:
+            out, xq, xs = r
+            outs.append(out)
+    return outs
+
+
+# ---- MXFP4 routed experts -------------------------------------------------------
+#
+# Codes are uint8 with two E2M1 values per byte (element 2i in the low
+# nibble), scales uint8 E8M0 with one byte per 32 values along K:
+# x_q [T, H/2] / x_scale [T, H/32], w13_q [E, 2I, H/2] / w13_scale
+# [E, 2I, H/32], w2_q [E, H, I/2] / w2_scale [E, H, I/32].
+
+
+def mxfp4_quantize(x, q=None, scale=None):
+    """BF16 [M, K] -> (codes uint8 [M, K/2], E8M0 scales uint8 [M, K/32]), one
+    power-of-two scale per 32 values: 2^(floor(log2 amax) - 2)."""
+    import torch
+
+    _want(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _want(q, torch.uint8, 2, "q")
+    _want(scale, torch.uint8, 2, "scale")
+    if tuple(q.shape) != (M, K // 2) or tuple(scale.shape) != (M, K // 32):
+        raise ValueError("output shapes do not match x")
+    _check("mxfp4_quantize", lib().mxfp4_quantize(x.data_ptr(), M, K, q.data_ptr(), scale.data_ptr(), _stream(x)))
+    return q, scale
+
+
+def _mx_dims(x_q, x_scale, topk_ids, w13_q, w13_scale):
+    import torch
+
+    for t, nd, n in ((x_q, 2, "x_q"), (x_scale, 2, "x_scale"), (w13_q, 3, "w13_q"), (w13_scale, 3, "w13_scale")):
+        _want(t, torch.uint8, nd, n)
+    T, Hh = x_q.shape
+    H = 2 * Hh
+    E, twoI, H2 = w13_q.shape
+    if 2 * H2 != H or twoI % 2 or tuple(x_scale.shape) != (T, H // 32) or tuple(w13_scale.shape) != (E, twoI, H // 32):
+        raise ValueError("x_q [T, H/2], x_scale [T, H/32], w13_q [E, 2I, H/2], w13_scale [E, 2I, H/32] expected")
+    k = topk_ids.shape[1] if topk_ids is not None else None
+    if topk_ids is not None and topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must be [T, k]")
+    return T, H, twoI // 2, E, k
+
+
+def moe_mxfp4_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int, order: int = 0):
+    """Sorted-slot gate/up rows of the MXFP4 product in BF16: [T*k, 2I]."""
+    import torch
+
+    T, H, I, E, _ = _mx_dims(x_q, x_scale, None, w13_q, w13_scale)
+    _check_order(offsets, E, topk, order)
+    gu = torch.empty((T * topk, 2 * I), dtype=torch.bfloat16, device=x_q.device)
+    _check("moe_mxfp4_gate_up_bf16", lib().moe_mxfp4_gate_up_bf16(
+        x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), w13_q.data_ptr(),
+        w13_scale.data_ptr(), gu.data_ptr(), T, H, I, E, topk, order, _stream(x_q)))
+    return gu
+
+
+def moe_mxfp4_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int, order: int = 0,
+                                   dst_row=None):
+    """MXFP4 h = silu(g) * u of every routed slot: (h_q uint8 [T*k, I/2], h_scale uint8 [T*k, I/32]),
+    on the sorted row of ``perm`` or on ``dst_row[slot]`` when given."""
+    import torch
+
+    T, H, I, E, _ = _mx_dims(x_q, x_scale, None, w13_q, w13_scale)
+    _check_order(offsets, E, topk, order)
+    if dst_row is not None:
+        _want(dst_row, torch.int32, 1, "dst_row")
+        if dst_row.numel() != T * topk:
+            raise ValueError("dst_row must have T * topk entries")
+    h_q = torch.empty((T * topk, I // 2), dtype=torch.uint8, device=x_q.device)
+    h_s = torch.empty((T * topk, I // 32), dtype=torch.uint8, device=x_q.device)
+    _check("moe_mxfp4_gate_up_swiglu_quant", lib().moe_mxfp4_gate_up_swiglu_quant(
+        x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(),
+        dst_row.data_ptr() if dst_row is not None else None, w13_q.data_ptr(), w13_scale.data_ptr(),
+        h_q.data_ptr(), h_s.data_ptr(), T, H, I, E, topk, order, _stream(x_q)))
+    return h_q, h_s
+
+
+def moe_mxfp4_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, order: int = 0,
+                           out=None, y=None, quantize_output=False):
+    """MXFP4 down projection and combine: BF16 [T, H], or (out, out_q, out_scale)
+    with ``quantize_output`` (the MXFP4 version of out, made in the combine)."""
+    import torch
+
+    T, k = topk_w.shape
+    E, H, Ih = w2_q.shape
+    I = 2 * Ih
+    _check_order(offsets, E, k, order)
+    _want(topk_ids, torch.int32, 2, "topk_ids")
+    if tuple(topk_ids.shape) != (T, k) or tuple(w2_scale.shape) != (E, H, I // 32):
+        raise ValueError("topk_ids [T, k] and w2_scale [E, H, I/32] expected")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
+    if y is None:
+        y = torch.empty((T * k, H), dtype=torch.float32, device=h_q.device)
+    if y.numel() < T * k * H or y.dtype != torch.float32:
+        raise ValueError("y must be float32 with at least T * k * H elements")
+    oq = os_ = None
+    if quantize_output:
+        oq = torch.empty((T, H // 2), dtype=torch.uint8, device=h_q.device)
+        os_ = torch.empty((T, H // 32), dtype=torch.uint8, device=h_q.device)
+    _check("moe_mxfp4_down_combine", lib().moe_mxfp4_down_combine(
+        h_q.data_ptr(), h_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), topk_ids.data_ptr(),
+        topk_w.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), y.data_ptr(),
+        oq.data_ptr() if quantize_output else None, os_.data_ptr() if quantize_output else None, T, H, I, E, k,
+        order, _stream(h_q)))
+    return (out, oq, os_) if quantize_output else out
+
+
+def moe_mxfp4_workspace(T: int, H: int, I: int, E: int, topk: int, device="cuda"):
+    """Scratch buffer sized for moe_mxfp4_grouped."""
+    import torch
+
+    nbytes = int(lib().moe_mxfp4_workspace_bytes(T, H, I, E, topk))
+    if nbytes == 0 and T > 0:
+        raise ValueError("unsupported routed-expert sizes")
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def moe_mxfp4_grouped(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out=None, workspace=None,
+                      quantize_output=False):
+    """One MXFP4 routed-expert pass: BF16 [T, H], or (out, out_q, out_scale) with
+    ``quantize_output`` (the MXFP4 input of the next pass)."""
+    import torch
+
+    _want(topk_ids, torch.int32, 2, "topk_ids")
+    _want(topk_w, torch.float32, 2, "topk_w")
+    _want(w2_q, torch.uint8, 3, "w2_q")
+    _want(w2_scale, torch.uint8, 3, "w2_scale")
+    T, H, I, E, k = _mx_dims(x_q, x_scale, topk_ids, w13_q, w13_scale)
+    if tuple(w2_q.shape) != (E, H, I // 2) or tuple(w2_scale.shape) != (E, H, I // 32) or tuple(topk_w.shape) != (T, k):
+        raise ValueError("w2_q [E, H, I/2], w2_scale [E, H, I/32] and topk_w [T, k] expected")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x_q.device)
+    if workspace is None:
+        workspace = moe_mxfp4_workspace(T, H, I, E, k, device=x_q.device)
+    oq = os_ = None
+    if quantize_output:
+        oq = torch.empty((T, H // 2), dtype=torch.uint8, device=x_q.device)
+        os_ = torch.empty((T, H // 32), dtype=torch.uint8, device=x_q.device)
+    _check("moe_mxfp4_grouped", lib().moe_mxfp4_grouped(
+        x_q.data_ptr(), x_scale.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w13_q.data_ptr(),
+        w13_scale.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(),
+        oq.data_ptr() if quantize_output else None, os_.data_ptr() if quantize_output else None, T, H, I, E, k,
+        workspace.data_ptr(), workspace.numel(), _stream(x_q)))
+    return (out, oq, os_) if quantize_output else out
+
+
+def moe_mxfp4_ffn(x, routes, w13_q, w13_scale, w2_q, w2_scale, workspace=None):
+    """The MXFP4 routed-expert stage run once per entry of ``routes`` on one set of
+    weights, each pass fed the previous pass's output (quantised in its combine).
+    Returns the list of per-pass BF16 outputs."""
+    outs = []
+    xq, xs = mxfp4_quantize(x)
+    for i, (ids, w) in enumerate(routes):
+        last = i + 1 == len(routes)
+        r = moe_mxfp4_grouped(xq, xs, ids, w, w13_q, w13_scale, w2_q, w2_scale, workspace=workspace,
+                              quantize_output=not last)
         if last:
             outs.append(r)
         else:

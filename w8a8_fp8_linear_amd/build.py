@@ -12,7 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "w8a16.hip", "moe.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "w8a16.hip", "moe.hip", "mx.hip"]
 OUT = os.path.join(HERE, "libw8a8.so")
 
 FLAGS = [

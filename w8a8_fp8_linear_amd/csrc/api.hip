@@ -320,3 +320,110 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
 }
 
 }  // extern "C"
+
+// ---- MXFP4 routed experts -----------------------------------------------------
+namespace {
+
+constexpr int64_t kMxMultiple = 128;  // one FP4 matrix-core step along K; a gate/up tile holds 128 h columns
+
+int check_mx_moe(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order) {
+  const int c = check_moe_shape(T, H, I, E, topk);
+  if (c != W8A8_OK) return c;
+  if (H % kMxMultiple != 0 || I % kMxMultiple != 0) return W8A8_ERR_UNSUPPORTED;
+  if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
+  if (!mul_ok(T * topk, H) || !mul_ok(T * topk * H, 4)) return W8A8_ERR_BAD_SHAPE;
+  return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_quantize(const uint16_t* x_bf16, int64_t M, int64_t K, uint8_t* q_fp4, uint8_t* scale_e8m0,
+                   hipStream_t stream) {
+  if (M < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(M * K, 2)) return W8A8_ERR_BAD_SHAPE;
+  if (K == 0 || K % 32 != 0 || K > (int64_t(1) << 24)) return W8A8_ERR_UNSUPPORTED;
+  if (M * K / 8 >= (int64_t(1) << 40)) return W8A8_ERR_UNSUPPORTED;
+  if (M == 0) return W8A8_OK;
+  if (any_null({x_bf16, q_fp4, scale_e8m0})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_bf16, q_fp4, scale_e8m0})) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_mx_quantize(x_bf16, M, K, q_fp4, scale_e8m0, stream));
+}
+
+int moe_mxfp4_gate_up_bf16(const uint8_t* x_q, const uint8_t* x_scale, const int32_t* perm, const int32_t* offsets,
+                           const uint8_t* w13_q, const uint8_t* w13_scale, uint16_t* gu_bf16, int64_t T, int64_t H,
+                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
+  const int c = check_mx_moe(T, H, I, E, topk, order);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16})) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_mx_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, gu_bf16, T, H, I, E,
+                                                    topk, order, stream));
+}
+
+int moe_mxfp4_gate_up_swiglu_quant(const uint8_t* x_q, const uint8_t* x_scale, const int32_t* perm,
+                                   const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13_q,
+                                   const uint8_t* w13_scale, uint8_t* h_q, uint8_t* h_scale, int64_t T, int64_t H,
+                                   int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
+  const int c = check_mx_moe(T, H, I, E, topk, order);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale})) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale, h_q, h_scale}))
+    return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_mx_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale,
+                                                            h_q, h_scale, T, H, I, E, topk, order, stream));
+}
+
+int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int32_t* perm, const int32_t* offsets,
+                           const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const uint8_t* w2_scale,
+                           uint16_t* out_bf16, float* y_f32, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
+                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
+  const int c = check_mx_moe(T, H, I, E, topk, order);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
+    return W8A8_ERR_NULL_ARG;
+  if ((out_q == nullptr) != (out_scale == nullptr)) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32, out_q, out_scale}))
+    return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_mx_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
+                                                    out_bf16, y_f32, out_q, out_scale, T, H, I, E, topk, order,
+                                                    stream));
+}
+
+size_t moe_mxfp4_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+  if (check_mx_moe(T, H, I, E, topk, 0) != W8A8_OK) return 0;
+  return w8a8::mx_moe_workspace_bytes(T, H, I, E, topk);
+}
+
+int moe_mxfp4_grouped(const uint8_t* x_q, const uint8_t* x_scale, const int32_t* topk_ids, const float* topk_w,
+                      const uint8_t* w13_q, const uint8_t* w13_scale, const uint8_t* w2_q, const uint8_t* w2_scale,
+                      uint16_t* out_bf16, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H, int64_t I,
+                      int64_t E, int64_t topk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int c = check_mx_moe(T, H, I, E, topk, 0);
+  if (c != W8A8_OK) return c;
+  if (T == 0) return W8A8_OK;
+  if (any_null({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, workspace}))
+    return W8A8_ERR_NULL_ARG;
+  if ((out_q == nullptr) != (out_scale == nullptr)) return W8A8_ERR_NULL_ARG;
+  if (!all_aligned({x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16, out_q, out_scale,
+                    workspace}))
+    return W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < w8a8::mx_moe_workspace_bytes(T, H, I, E, topk)) return W8A8_ERR_WORKSPACE;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_mx_moe(x_q, x_scale, topk_ids, topk_w, w13_q, w13_scale, w2_q, w2_scale, out_bf16,
+                                           out_q, out_scale, T, H, I, E, topk, workspace, stream));
+}
+
+}  // extern "C"

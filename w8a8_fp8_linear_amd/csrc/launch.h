@@ -68,4 +68,32 @@ hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, co
                       uint16_t* out, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I,
                       int64_t E, int64_t topk, void* ws, hipStream_t stream);
 
+// MXFP4 routed experts (mx.hip): codes [rows, K/2] (two E2M1 per byte, the
+// even element in the low nibble) and E8M0 scales [rows, K/32]. The grouped
+// calls need H % 128 == 0 and I % 128 == 0.
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s, hipStream_t stream);
+
+hipError_t launch_mx_gate_up_bf16(const uint8_t* xq, const uint8_t* xs, const int32_t* perm, const int32_t* offsets,
+                                  const uint8_t* w13, const uint8_t* s13, uint16_t* gu, int64_t T, int64_t H,
+                                  int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, const int32_t* perm,
+                                          const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
+                                          const uint8_t* s13, uint8_t* qh, uint8_t* sh, int64_t T, int64_t H,
+                                          int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+// y: [T*topk, H] float32 scratch; out_q / out_s (both NULL or both set): also
+// the MXFP4 quantisation of out.
+hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
+                                  const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
+                                  uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
+                                  int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+
+size_t mx_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
+
+hipError_t launch_mx_moe(const uint8_t* xq, const uint8_t* xs, const int32_t* ids, const float* tw,
+                         const uint8_t* w13, const uint8_t* s13, const uint8_t* w2, const uint8_t* s2, uint16_t* out,
+                         uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                         void* ws, hipStream_t stream);
+
 }  // namespace w8a8

@@ -46,6 +46,7 @@
 #include <algorithm>
 
 #include "device.h"
+#include "grouped.h"
 #include "launch.h"
 
 namespace w8a8 {
@@ -194,46 +195,6 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
     if (leader && key < E) base[wave * E + key] += __popcll(peers);
     __builtin_amdgcn_wave_barrier();
   }
-}
-
-// Which expert and which rows the m-tile `mt` covers, from the device-side
-// offsets (each wave computes it; the answer is uniform). The rows are
-// clamped to [0, cap), the capacity of the sorted arrays, so inconsistent
-// offsets can never address outside them.
-__device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int BM, int mt, int cap, int& e_out,
-                                 int& row0, int& rows) {
-  const int lane = threadIdx.x & 63;
-  int acc = 0;
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int e = e0 + lane;
-    int cnt = 0, start = 0;
-    if (e < E) {
-      start = offsets[e];
-      cnt = offsets[e + 1] - start;
-    }
-    const int tiles = (cnt + BM - 1) / BM;
-    int incl = tiles;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
-    }
-    const int excl = incl - tiles;
-    const bool hit = e < E && mt >= acc + excl && mt < acc + incl;
-    const uint64_t b = __ballot(hit);
-    if (b) {
-      const int src = __ffsll((unsigned long long)b) - 1;
-      const int ex = __shfl(excl, src, 64), st = __shfl(start, src, 64), ct = __shfl(cnt, src, 64);
-      const int local = mt - acc - ex;
-      e_out = __builtin_amdgcn_readfirstlane(e0 + src);
-      row0 = __builtin_amdgcn_readfirstlane(st + local * BM);
-      rows = __builtin_amdgcn_readfirstlane(min(BM, ct - local * BM));
-      if (row0 < 0 || row0 >= cap) return false;
-      rows = min(rows, cap - row0);
-      return rows > 0;
-    }
-    acc += __shfl(incl, 63, 64);
-  }
-  return false;
 }
 
 enum { kGateUp = 0, kGateUpH = 1, kDownY = 2 };
@@ -553,44 +514,6 @@ __global__ __launch_bounds__(256) void requant_rows(const float* __restrict__ h,
 __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0u;
-}
-
-// Sum of a token's valid slot rows at columns c0 .. c0 + 7, in the order
-// j = 0, 1, ... in float32 (deterministic). The k rows of a token are
-// contiguous in y; they are loaded (non-temporal: each byte is read once;
-// measured 8% faster on this stage) before any is added, and a dropped
-// slot's row is read but not used.
-__device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __restrict__ ids, int64_t t, int topk,
-                                  int Eids, int H, int c0, float4& a, float4& b) {
-  a = make_float4(0.f, 0.f, 0.f, 0.f);
-  b = a;
-  constexpr int kBatch = 8;
-  for (int j0 = 0; j0 < topk; j0 += kBatch) {
-    float4 u[kBatch], v[kBatch];
-    bool ok[kBatch];
-#pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      const int j = j0 + jj;
-      const int64_t slot = t * topk + (j < topk ? j : 0);
-      const int id = ids[slot];
-      ok[jj] = j < topk && id >= 0 && id < Eids;
-      const v4f* src = reinterpret_cast<const v4f*>(y + slot * H + c0);
-      const v4f t0 = __builtin_nontemporal_load(src), t1 = __builtin_nontemporal_load(src + 1);
-      u[jj] = make_float4(t0[0], t0[1], t0[2], t0[3]);
-      v[jj] = make_float4(t1[0], t1[1], t1[2], t1[3]);
-    }
-#pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      if (!ok[jj]) continue;
-      a.x += u[jj].x; a.y += u[jj].y; a.z += u[jj].z; a.w += u[jj].w;
-      b.x += v[jj].x; b.y += v[jj].y; b.z += v[jj].z; b.w += v[jj].w;
-    }
-  }
-}
-
-__device__ inline uint4 to_bf16x8(float4 a, float4 b) {
-  return make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16), f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
-                    f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16), f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
 }
 
 // out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots.
