@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
+FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 (MXFP4) MFMA
 METRIC = "W8A8 TFLOP/s & % FP8 MFMA peak (prefill M=4096); HBM GB/s at decode M=8"
 
 
@@ -405,6 +406,81 @@ def bench_moe_pages_shapes(reps=10, warmup=3):
     return out
 
 
+def _mx_inputs(cfg):
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    d = synth.moe_workload(**cfg, seed=0)
+    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+    x = _bf16_dev(d["x"])
+    q13, s13 = w8.mxfp4_quantize(_bf16_dev(d["w13"].reshape(E * 2 * I, H)))
+    q2, s2 = w8.mxfp4_quantize(_bf16_dev(d["w2"].reshape(E * H, I)))
+    routes = [(torch.from_numpy(i).cuda(), torch.from_numpy(w).cuda()) for i, w in d["routes"]]
+    return (x, q13.view(E, 2 * I, H // 2), s13.view(E, 2 * I, H // 32), q2.view(E, H, I // 2),
+            s2.view(E, H, I // 32), routes)
+
+
+def bench_moe_mxfp4(reps=10, warmup=3):
+    """The two-pass routed-expert FFN with MXFP4 experts (E2M1 values, one E8M0
+    scale per 32 inputs, the FP4 matrix cores), on the 16384-token workload
+    (with a per-stage split of one pass) and at the pages' expert shapes."""
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for cfg in (synth.MOE_TWO_PASS, synth.MOE_PRAXIS, synth.MOE_LOGOS):
+        T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+        x, q13, s13, q2, s2, routes = _mx_inputs(cfg)
+        ws = w8.moe_mxfp4_workspace(T, H, I, E, k)
+        for _ in range(warmup):
+            w8.moe_mxfp4_ffn(x, routes, q13, s13, q2, s2, workspace=ws)
+        torch.cuda.synchronize()
+        evs = _events(reps)
+        for a, b in evs:
+            a.record(stream)
+            w8.moe_mxfp4_ffn(x, routes, q13, s13, q2, s2, workspace=ws)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = _avg_ms(evs)
+        flops = 2 * (2.0 * T * k * 2 * I * H + 2.0 * T * k * H * I)
+        rec = {"us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
+               "frac_fp4_peak": flops / (ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, "tokens_per_s": T / (ms * 1e-3)}
+        if cfg is synth.MOE_TWO_PASS:
+            xq, xs = w8.mxfp4_quantize(x)
+            ids, tw = routes[0]
+            _, off0, perm0 = w8.moe_route(ids, E, order=0)
+            hq, hs = w8.moe_mxfp4_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0)
+            o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+            stages = {}
+            for name, fn, fl in (
+                ("quantize", lambda: w8.mxfp4_quantize(x, xq, xs), 0),
+                ("route", lambda: w8.moe_route(ids, E, order=0), 0),
+                ("gate_up_swiglu_quant",
+                 lambda: w8.moe_mxfp4_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0),
+                 2.0 * T * k * 2 * I * H),
+                ("down_combine", lambda: w8.moe_mxfp4_down_combine(hq, hs, perm0, off0, ids, tw, q2, s2, order=0,
+                                                                   out=o, y=y), 2.0 * T * k * H * I),
+            ):
+                ev = _events(reps)
+                for a, b in ev:
+                    a.record(stream); fn(); b.record(stream)
+                torch.cuda.synchronize()
+                us = 1e3 * _avg_ms(ev)
+                stages[name] = us
+                if fl:
+                    stages[name + "_tflops"] = fl / (us * 1e-6) / 1e12
+            rec["stage_us_one_pass"] = stages
+        out[cfg["name"]] = rec
+        del x, q13, s13, q2, s2, routes, ws
+    return out
+
+
 def cpu_baseline():
     """The CPU oracle on the full prefill workload (activation quantisation,
     exact float64 GEMM, BF16 rounding), timed once on this host."""
@@ -466,7 +542,7 @@ def main():
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         dec = bench_decode()
-    moe_gu = moe_ffn = moe_pages = None
+    moe_gu = moe_ffn = moe_pages = moe_mx = None
     if not args.no_moe:
         print("[bench] routed gate/up", file=sys.stderr, flush=True)
         moe_gu = bench_moe_gate_up()
@@ -474,6 +550,8 @@ def main():
         moe_ffn = bench_moe_two_pass()
         print("[bench] routed FFN at the pages' expert shapes", file=sys.stderr, flush=True)
         moe_pages = bench_moe_pages_shapes()
+        print("[bench] routed FFN with MXFP4 experts", file=sys.stderr, flush=True)
+        moe_mx = bench_moe_mxfp4()
     dm = None
     if not args.no_default_maths:
         print("[bench] default maths (W8A16)", file=sys.stderr, flush=True)
@@ -513,6 +591,7 @@ def main():
         "moe_gate_up": moe_gu,
         "moe_two_pass": moe_ffn,
         "moe_pages_shapes": moe_pages,
+        "moe_mxfp4": moe_mx,
         "default_maths": dm,
         "cpu_baseline": cpu,
     }
