@@ -156,6 +156,44 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
     return out
 
 
+def bench_decode_layer(Ms=(9, 16, 32), n_buffers=40, reps=5):
+    """The fast-math decode layer from BF16 input: fp8_linear (per-token
+    quantisation launch + GEMM launch) against fp8_linear_single_launch (the
+    quantisation fused into the GEMM), HIP-graph replayed over 40 rotated
+    weight copies."""
+    import torch
+
+    import synth
+    import w8a8_fp8_linear_amd as w8
+
+    cfg = synth.DENSE_DECODE
+    N, K = cfg["N"], cfg["K"]
+    d = synth.dense_workload(M=1, K=K, N=N, seed=0)
+    wq0, ws0 = w8.quantize_weight(_bf16_dev(d["w"]))
+    wqs = [wq0.roll(i, dims=0).contiguous() for i in range(n_buffers)]
+    wss = [ws0.roll(i).contiguous() for i in range(n_buffers)]
+    stream = torch.cuda.current_stream()
+    out = {}
+    for M in Ms:
+        x = _bf16_dev(synth.dense_workload(M=M, K=K, N=N, seed=1)["x"])
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(int(w8.lib().fp8_linear_workspace_bytes(M, K)), dtype=torch.uint8, device="cuda")
+        rec = {}
+        for name, mk in (
+            ("two_launch_us", lambda j: (lambda: w8.fp8_linear(x, wqs[j], wss[j], fast_math=True, out=y,
+                                                               workspace=ws))),
+            ("single_launch_us", lambda j: (lambda: w8.fp8_linear_single_launch(x, wqs[j], wss[j], out=y))),
+        ):
+            launches = [mk(j) for j in range(n_buffers)]
+            for f in launches:
+                f()
+            torch.cuda.synchronize()
+            rounds, _ = _per_launch_ms(launches, reps, stream)
+            rec[name] = 1e3 * sum(rounds) / len(rounds)
+        out[f"M{M}"] = rec
+    return out
+
+
 def bench_default_maths(steps=50, warmup=10, Ms=(1, 8), n_buffers=40, reps=5):
     """The default maths (W8A16) against the FP8 multiply: the model page's
     fast-math comparison at a 4,096-token prompt, and the decode weight stream."""
@@ -538,10 +576,12 @@ def main():
         del src, dst
     print(f"[bench] prefill: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     pre = bench_prefill(args.steps, args.warmup)
-    dec = None
+    dec = dec_layer = None
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         dec = bench_decode()
+        print("[bench] decode layer: two launches against one", file=sys.stderr, flush=True)
+        dec_layer = bench_decode_layer()
     moe_gu = moe_ffn = moe_pages = moe_mx = None
     if not args.no_moe:
         print("[bench] routed gate/up", file=sys.stderr, flush=True)
@@ -588,6 +628,7 @@ def main():
         "quant_GBs": round(pre["quant_gbs"], 1),
         "tokens_per_s": round(pre["tokens_per_s"], 1),
         "decode": dec,
+        "decode_layer_fast_math": dec_layer,
         "moe_gate_up": moe_gu,
         "moe_two_pass": moe_ffn,
         "moe_pages_shapes": moe_pages,

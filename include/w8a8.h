@@ -156,6 +156,22 @@ size_t fp8_linear_workspace_bytes(int64_t M, int64_t K);
 int fp8_linear(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
                int64_t N, int64_t K, int fast_math, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fp8_linear_single_launch — the FP8 multiply of fp8_linear (per-token
+ * quantisation, then the scaled FP8 GEMM; Lernex/Metis-1.6-Logos-FP8, "What
+ * --fast-math does") in one kernel launch with no workspace, for the few-token
+ * steps: 1 <= M <= 32, K <= 2048. Every workgroup derives the row scales from
+ * the BF16 input it loads and quantises it in registers with the
+ * quantize_per_token rule, so the result is bit-identical to
+ * quantize_per_token followed by w8a8_gemm. Each workgroup quantises the whole
+ * input, which makes this slower than the two launches on MI355X; it is for
+ * callers that need a single launch.
+ *   x_bf16 [M, K], w_q [N, K] E4M3, w_scale [N], y_bf16 [M, N]
+ * Errors: as w8a16_gemm; UNSUPPORTED also for M > 32 or K > 2048.
+ */
+int fp8_linear_single_launch(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Routed experts
  *

@@ -109,6 +109,15 @@ def test_fp8_linear_argument_errors():
         assert f(P, P, P, P, 8, 16, 32, 1, None, 0, None) == DEV   # M <= 8: default maths, no workspace
         assert f(P, P, P, P, 64, 16, 32, 0, None, 0, None) == DEV  # flag off: default maths
         assert f(P, P, P, P, 64, 16, 32, 1, P, need, None) == DEV
+    g = w8.lib().fp8_linear_single_launch
+    assert g(P, P, P, P, 33, 16, 32, None) == UNSUP          # M <= 32
+    assert g(P, P, P, P, 16, 16, 2064, None) == UNSUP        # K <= 2048
+    assert g(P, P, P, P, 16, 16, 24, None) == UNSUP          # K % 16
+    assert g(P, P, P, P, 0, 16, 32, None) == OK
+    assert g(None, P, P, P, 16, 16, 32, None) == NULL
+    assert g(P, P, P, P + 2, 16, 16, 32, None) == MIS
+    if not torch.cuda.is_available():
+        assert g(P, P, P, P, 16, 16, 32, None) == DEV
 
 
 def test_mxfp4_quantize_argument_errors():

@@ -8,6 +8,9 @@
   the output layout).
 * fp8_linear takes the FP8 path (quantize_per_token + w8a8_gemm, bit for bit)
   only with fast_math and more than 8 tokens, and the default maths otherwise.
+* fp8_linear_single_launch (the quantisation fused into the decode GEMM,
+  M <= 32, K <= 2048) is bit-identical to the two-launch chain, on workload
+  rows and on zero, subnormal, huge and tie rows, and inside the E4M3 bound.
 """
 import numpy as np
 import pytest
@@ -102,3 +105,48 @@ def test_w8a16_argument_errors():
     with pytest.raises(w8.W8A8Error) as e:
         w8.w8a16_gemm(x, w, s)                    # K = 24 is not a multiple of 16
     assert e.value.status == 4
+
+
+def _special_decode_rows(M, K, rng):
+    """Rows that exercise the quantiser: zero, subnormal, tiny-negative, huge, ties of the E4M3 grid."""
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-10, 10, (M, 1)))).astype(np.float32)
+    x[0] = 0.0
+    if M > 1:
+        x[1] = 0.0
+        x[1, K // 3] = 3e-39                            # subnormal row maximum
+        x[1, 0] = -1e-40
+    if M > 2:
+        x[2, :] = 448.0 * np.sign(rng.standard_normal(K))
+        x[2, 5] = 3.38e38                              # near the largest BF16
+    if M > 3:
+        x[3, :] = rng.choice([0.5, 1.0625, 1.1875, -2.0625, 3.1e-3], K)   # E4M3 ties after scaling
+    return oracle.round_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 2048), (9, 8192, 2048), (16, 8192, 2048), (17, 8192, 2048),
+                                   (32, 8192, 2048), (13, 1040, 528), (24, 16, 16), (31, 48, 2048),
+                                   (12, 4096, 1024)])
+def test_single_launch_equals_chain(M, N, K):
+    """fp8_linear_single_launch is bit-identical to quantize_per_token + w8a8_gemm, and
+    inside the E4M3 matrix-core bound against the oracle."""
+    print(f"[fused decode] {M}x{N}x{K}", flush=True)
+    rng = np.random.default_rng(M * 7 + K)
+    d = synth.dense_workload(M=M, N=N, K=K, n_outlier=min(3, K), seed=M + N + K)
+    qw, sw = _weights(d)
+    wq, ws = to_dev(qw), to_dev(sw)
+    for bits in (d["x"], _special_decode_rows(M, K, rng)):
+        x = to_dev_bf16(bits)
+        fused = bf16_bits(w8.fp8_linear_single_launch(x, wq, ws))
+        q, s = w8.quantize_per_token(x)
+        chain = bf16_bits(w8.w8a8_gemm(q, s, wq, ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(fused, chain)
+    from gpu_util import gemm_report
+    x32 = synth.bf16_bits_to_f32(d["x"])
+    qx, sx, _ = oracle.quantize_rows(x32)
+    fused = bf16_bits(w8.fp8_linear_single_launch(to_dev_bf16(d["x"]), wq, ws))
+    torch.cuda.synchronize()
+    rep = gemm_report(fused, qx, sx, qw, sw)
+    record(f"fp8_linear_single_launch {M}x{N}x{K}", rep)
+    assert rep["n_bound_violations"] == 0, rep
+    assert rep["frobenius"] <= 4e-3, rep

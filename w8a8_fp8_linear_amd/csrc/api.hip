@@ -149,6 +149,19 @@ int fp8_linear(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale,
   return launch_status(w8a8::launch_gemm(xq, xs, w_q, w_scale, y_bf16, M, N, K, stream));
 }
 
+int fp8_linear_single_launch(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int c = check_dense_shape(M, N, K);
+  if (c != W8A8_OK) return c;
+  if (M > w8a8::kFusedDecodeMaxM || K > w8a8::kFusedDecodeMaxK) return W8A8_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!x_bf16 || !w_q || !w_scale || !y_bf16) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_bf16)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_quant_gemm_decode(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
+}
+
 }  // extern "C"
 
 // ---- routed experts ---------------------------------------------------------

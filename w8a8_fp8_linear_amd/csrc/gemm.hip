@@ -23,6 +23,17 @@
 //    split K, each lane loads its MFMA operands straight from global memory
 //    with 16-byte loads (every weight byte is read once), and the partial
 //    sums meet in LDS.
+//  * gemm_skinny_q: gemm_skinny with the per-token quantisation of its BF16
+//    input fused in (one launch instead of two). For K <= 2048 one round of
+//    the skinny loop covers all of K, so the 4 waves of a workgroup load
+//    every input element exactly once, as BF16; each lane folds the
+//    magnitudes of its chunks into per-row maxima, the maxima meet over the
+//    lane groups (shuffles) and the waves (LDS), and each lane then
+//    quantises its own chunks with the per-token rule, the same code as
+//    quantize_per_token, so the codes and the result are identical to the
+//    two-launch chain. Every workgroup quantises the whole input (no
+//    workgroup can see another's codes without a grid-wide barrier), which
+//    costs more vector-ALU time than the separate quantisation launch saves.
 //
 // Within one 128-byte K slice, lane group g (lane / 16) of an MFMA operand
 // holds the 16-byte chunks g and g + 4 of its row. A and W use the same
@@ -226,6 +237,106 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
   }
 }
 
+// Fused decode: X BF16 [M, K] with M <= 16 * MT and K <= 512 * U (one round).
+template <int MT, int U>
+__global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W,
+                                                     const float* __restrict__ sw, uint16_t* __restrict__ Y, int M,
+                                                     int N, int K) {
+  __shared__ v4f red[3][MT][64];
+  __shared__ uint32_t wmax[4][MT * 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 16;
+  const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  const auto rX = make_rsrc(X, (int64_t)M * K * 2);
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t wrow = (uint32_t)r16 * (uint32_t)K;
+  const int nk = (K + 127) >> 7;
+  // Weights first (their latency is the longest), then this wave's BF16
+  // chunks: for K slice kt = wave + 4u, elements [128 kt + 16 g, +16) and
+  // [128 kt + 64 + 16 g, +16) of each row, 32 bytes each.
+  v8i wf[U];
+  uint4 xb[U][MT][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k0 = (wave + 4 * u) << 7;
+    const int c0 = k0 + 16 * g, c1 = c0 + 64;
+    const bool live = wave + 4 * u < nk;
+    const uint32_t o0 = (live && c0 < K) ? (uint32_t)c0 : kOutOfRange;
+    const uint32_t o1 = (live && c1 < K) ? (uint32_t)c1 : kOutOfRange;
+    const v4i lo = buffer_load16(rW, o0 == kOutOfRange ? o0 : wrow + o0);
+    const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
+    wf[u] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint32_t xrow = (uint32_t)(t * 16 + r16) * (uint32_t)K * 2u;
+      const uint32_t b0 = o0 == kOutOfRange ? o0 : xrow + 2u * o0;
+      const uint32_t b1 = o1 == kOutOfRange ? o1 : xrow + 2u * o1;
+      const v4i a0 = buffer_load16(rX, b0), a1 = buffer_load16(rX, b0 == kOutOfRange ? b0 : b0 + 16u);
+      const v4i a2 = buffer_load16(rX, b1), a3 = buffer_load16(rX, b1 == kOutOfRange ? b1 : b1 + 16u);
+      xb[u][t][0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+      xb[u][t][1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
+      xb[u][t][2] = make_uint4(a2.x, a2.y, a2.z, a2.w);
+      xb[u][t][3] = make_uint4(a3.x, a3.y, a3.z, a3.w);
+    }
+  }
+  // Row maxima of |x| (integer max on the BF16 bits, as quantize_per_token).
+  uint32_t am[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    am[t] = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) am[t] = max(am[t], absmax8(xb[u][t][c]));
+    am[t] = max(am[t], (uint32_t)__shfl_xor((int)am[t], 16, 64));
+    am[t] = max(am[t], (uint32_t)__shfl_xor((int)am[t], 32, 64));
+    if (g == 0) wmax[wave][t * 16 + r16] = am[t];
+  }
+  __syncthreads();
+  float s[MT], r[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int row = t * 16 + r16;
+    const uint32_t a = max(max(wmax[0][row], wmax[1][row]), max(wmax[2][row], wmax[3][row]));
+    s[t] = row_scale(a);
+    r[t] = 1.0f / s[t];
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint2 q0 = quant8(xb[u][t][0], s[t], r[t]), q1 = quant8(xb[u][t][1], s[t], r[t]);
+      const uint2 q2 = quant8(xb[u][t][2], s[t], r[t]), q3 = quant8(xb[u][t][3], s[t], r[t]);
+      const v8i xf = v8i{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, (int)q3.x, (int)q3.y};
+      acc[t] = mfma_16x16x128_e4m3(wf[u], xf, acc[t]);
+    }
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int n = n0 + 4 * g;
+  if (n >= N) return;
+  const float4 sW = *reinterpret_cast<const float4*>(sw + n);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
+    const int m = t * 16 + r16;
+    if (m < M) {
+      const uint32_t b0 = f32_to_bf16_rne(a[0] * s[t] * sW.x);
+      const uint32_t b1 = f32_to_bf16_rne(a[1] * s[t] * sW.y);
+      const uint32_t b2 = f32_to_bf16_rne(a[2] * s[t] * sW.z);
+      const uint32_t b3 = f32_to_bf16_rne(a[3] * s[t] * sW.w);
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t run_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -251,6 +362,17 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
     return hipGetLastError();
   }
   return run_tiled<256, 192, 2, 4>(a, sa, w, sw, y, M, N, K, stream);
+}
+
+hipError_t launch_quant_gemm_decode(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
+                                    int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const dim3 grid((unsigned)((N + 15) / 16));
+  if (M <= 16)
+    hipLaunchKernelGGL((gemm_skinny_q<1, 4>), grid, dim3(256), 0, stream, x, w, sw, y, (int)M, (int)N, (int)K);
+  else
+    hipLaunchKernelGGL((gemm_skinny_q<2, 4>), grid, dim3(256), 0, stream, x, w, sw, y, (int)M, (int)N, (int)K);
+  return hipGetLastError();
 }
 
 }  // namespace w8a8

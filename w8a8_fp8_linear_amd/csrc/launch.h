@@ -16,6 +16,13 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                        uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Per-token quantisation fused into the decode GEMM (one launch), for
+// M <= kFusedDecodeMaxM and K <= kFusedDecodeMaxK; bit-identical to
+// launch_quantize_rows followed by launch_gemm.
+constexpr int64_t kFusedDecodeMaxM = 32, kFusedDecodeMaxK = 2048;
+hipError_t launch_quant_gemm_decode(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
+                                    int64_t N, int64_t K, hipStream_t stream);
+
 // Default maths (w8a16.hip): y[m,n] = bf16(sw[n] * sum_k x[m,k] w[n,k]), x BF16,
 // w E4M3 widened to BF16, BF16 MFMA.
 hipError_t launch_w8a16_gemm(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y,
