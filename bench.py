@@ -52,6 +52,42 @@ GEMM_PREFILL_TRAFFIC = {"kernel": "gemm_tiled<256,192,2,4>", "bytes": (41097 * 2
 GEMM_PREFILL_KERNEL = "gemm_tiled<256,192,2,4>"
 
 
+def _library_reference(xq, xs, wq, ws, reps=20):
+    """Context, not a target: the vendor library's FP8 GEMM with the same
+    row-wise scales on the same operands (torch._scaled_mm, hipBLASLt),
+    HIP-graph timed. None if the library refuses the call."""
+    import torch
+
+    try:
+        a = xq.view(torch.float8_e4m3fn)
+        b = wq.view(torch.float8_e4m3fn)
+        sa, sb = xs.view(-1, 1), ws.view(1, -1)
+        f = lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps
+            best = t if best is None else min(best, t)
+        M, K = xq.shape
+        N = wq.shape[0]
+        return {"what": "torch._scaled_mm (hipBLASLt), FP8 E4M3, row-wise scales, BF16 out, same operands",
+                "us": 1e3 * best, "tflops": 2.0 * M * N * K / (best * 1e-3) / 1e12}
+    except Exception as e:  # pragma: no cover - depends on the installed library
+        return {"what": "torch._scaled_mm (hipBLASLt)", "error": repr(e)[:200]}
+
+
 def bench_prefill(steps, warmup):
     import torch
 
@@ -75,12 +111,35 @@ def bench_prefill(steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # Eager: `steps` Python-launched steps (the host's launch rate can bound this).
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
+    wall_eager = time.perf_counter() - t0
+    # The timed figure: the same `steps` steps captured once into a HIP graph
+    # (every launch of the hot path, nothing skipped) and replayed once between
+    # two synchronisations, as a serving loop would run them.
+    wall, timing = wall_eager, "eager launches"
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                step()
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        wall, timing = best, "one HIP-graph replay of all steps (best of 3)"
+        del g
+    except RuntimeError:
+        torch.cuda.synchronize()
     # Each kernel's average launch duration: `steps` back-to-back launches on
     # the same stream between two HIP events, repeated `rounds` times.
     def launches_ms(fn, rounds=5):
@@ -104,7 +163,9 @@ def bench_prefill(steps, warmup):
     gemm_bytes = M * K + N * K + 2 * M * N + 4 * (M + N)
     q_bytes = 2 * M * K + M * K + 4 * M
     return {
-        "M": M, "N": N, "K": K, "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
+        "M": M, "N": N, "K": K, "wall_s": wall, "ms_per_step": 1e3 * wall / steps, "step_timing": timing,
+        "ms_per_step_eager": 1e3 * wall_eager / steps,
+        "library_reference": _library_reference(xq, xs, wq, ws),
         "tflops": flops * steps / wall / 1e12,
         "gemm_ms_avg": gemm_avg, "gemm_ms_min": gemm_ms[0], "gemm_ms_max": gemm_ms[-1],
         "gemm_tflops": flops / (gemm_avg * 1e-3) / 1e12, "gemm_flops": flops, "gemm_bytes": gemm_bytes,
@@ -391,7 +452,7 @@ def bench_moe_two_pass(reps=5, warmup=2):
                         device="cuda")
     hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0, workspace=gu_ws)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
     for name, fn, fl in (
         ("gate_up_swiglu_quant", lambda: w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0,
                                                                      workspace=gu_ws),
@@ -494,7 +555,7 @@ def bench_moe_mxfp4(reps=10, warmup=3):
             _, off0, perm0 = w8.moe_route(ids, E, order=0)
             hq, hs = w8.moe_mxfp4_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0)
             o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-            y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+            y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
             stages = {}
             for name, fn, fl in (
                 ("quantize", lambda: w8.mxfp4_quantize(x, xq, xs), 0),
@@ -622,6 +683,9 @@ def main():
                                  if GEMM_PREFILL_TRAFFIC["kernel"] == GEMM_PREFILL_KERNEL else None),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": pre["gemm_bytes"]},
+        "step_timing": pre["step_timing"],
+        "ms_per_step_eager_launches": round(pre["ms_per_step_eager"], 5),
+        "library_reference": pre["library_reference"],
         "gemm_us_avg": round(pre["gemm_ms_avg"] * 1e3, 3),
         "gemm_us_min_max_of_rounds": [round(pre["gemm_ms_min"] * 1e3, 3), round(pre["gemm_ms_max"] * 1e3, 3)],
         "quant_us_avg": round(pre["quant_ms_avg"] * 1e3, 3),

@@ -180,11 +180,13 @@ int fp8_linear_single_launch(const uint16_t* x_bf16, const uint8_t* w_q, const f
  * Praxis, "Architecture"); experts are stacked in global expert order (the
  * "Files" section of the model pages); the stack, and so this expert stage,
  * runs twice per token with one set of weights (sglang-metis 0.1.0, "How the
- * model maps onto SGLang"). Readings taken where the pages are silent: W13[e]
- * holds [gate; up] rows, the activation is h = silu(g) * u in float32, h is
- * requantised with one E4M3 scale per routed copy, the k outputs of a token
- * are weighted by its router weights, summed in float32 and rounded once to
- * BF16.
+ * model maps onto SGLang"). Readings taken where the pages are silent:
+ * W13[e] holds [gate; up] rows; h = silu(g) * u in float32; h is requantised
+ * with one E4M3 scale per routed copy; each routed copy's output, weighted
+ * by its router weight, is rounded to BF16 (the model's dtype between the
+ * expert stage and the top-k sum, as in the fused-MoE kernels the model is
+ * built on: sglang-metis 0.1.0, the package description); the k BF16
+ * outputs of a token are summed in float32 and rounded once to BF16.
  *
  * Shapes (all row-major)
  *   x_q      [T, H]       E4M3 tokens, quantised once per token (quantize_per_token)
@@ -265,18 +267,18 @@ int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int
 
 /*
  * moe_down_combine — grouped down projection and router-weighted combine:
- *   y[slot, :]   = topk_w[slot] * h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T)
- *                  for the slot of sorted row r (float32)
+ *   y[slot, :]   = bf16( topk_w[slot] * h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T) )
+ *                  for the slot of sorted row r (product and scaling in float32)
  *   out_bf16[t]  = bf16( sum over j = 0..topk-1 with a valid id of y[t*topk + j] )
  * The sum is float32 and always taken in the order j = 0, 1, ... (so the
  * result does not depend on the sorted order and is deterministic).
  * perm/offsets may be in either order (`order`); topk_ids tells the valid
- * slots. y_f32 [T*topk, H] is caller-provided float32 scratch. A token with
+ * slots. y_bf16 [T*topk, H] is caller-provided BF16 scratch. A token with
  * no valid slot gets zeros.
  */
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
                      const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const float* w2_scale,
-                     uint16_t* out_bf16, float* y_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     uint16_t* out_bf16, uint16_t* y_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                      int order, hipStream_t stream);
 
 /* Bytes of scratch w8a8_grouped_gemm needs (0 for invalid sizes). */
@@ -337,9 +339,9 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
  *
  * The expert chain is that of the FP8 calls above with every expert input
  * and weight in MXFP4: tokens are quantised once over H, h = silu(g) * u
- * (float32) is quantised per routed copy over I, y = topk_w * product, and
- * the k outputs of a token are summed in float32 in the order j = 0, 1, ...
- * and rounded once to BF16.
+ * (float32) is quantised per routed copy over I, y = bf16(topk_w * product),
+ * and the k BF16 outputs of a token are summed in float32 in the order
+ * j = 0, 1, ... and rounded once to BF16.
  * Shapes: x_q [T, H/2] / x_scale [T, H/32]; w13_q [E, 2I, H/2] /
  * w13_scale [E, 2I, H/32] (rows 0..I-1 gate, I..2I-1 up); w2_q [E, H, I/2] /
  * w2_scale [E, H, I/32]; h_q [T*topk, I/2] / h_scale [T*topk, I/32].
@@ -383,16 +385,17 @@ int moe_mxfp4_gate_up_swiglu_quant(const uint8_t* x_q, const uint8_t* x_scale, c
 
 /*
  * moe_mxfp4_down_combine — grouped down projection and combine:
- *   y[slot, :]  = topk_w[slot] * (h[r] . W2[e]^T)   (float32, sorted row r)
+ *   y[slot, :]  = bf16( topk_w[slot] * (h[r] . W2[e]^T) )   (sorted row r)
  *   out_bf16[t] = bf16( sum over valid j, in order j = 0, 1, ... of y[t*topk + j] )
- *   y_f32 [T*topk, H] is caller-provided float32 scratch.
+ *                 (float32 sum)
+ *   y_bf16 [T*topk, H] is caller-provided BF16 scratch.
  *   out_q [T, H/2], out_scale [T, H/32]  optional (both NULL or both set):
  *               mxfp4_quantize(out_bf16), bit for bit, fused into the
  *               combine — the next pass's expert input.
  */
 int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int32_t* perm, const int32_t* offsets,
                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const uint8_t* w2_scale,
-                           uint16_t* out_bf16, float* y_f32, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
+                           uint16_t* out_bf16, uint16_t* y_bf16, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
                            int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
 /* Bytes of scratch moe_mxfp4_grouped needs (0 for invalid sizes). */

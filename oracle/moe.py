@@ -20,10 +20,13 @@ design notes):
 * Each token is quantised once over H; its k routed copies share that
   scale. h is rounded to float32 (not BF16) and requantised per routed
   copy (slot) with the same per-row quantiser.
-* The down projection W2[e] is [H, I]; each slot's output is scaled by its
-  router weight, the k weighted outputs of a token are summed in float64
-  and rounded once to BF16. Router weights are inputs and are not
-  renormalised here.
+* The down projection W2[e] is [H, I]; each slot's output, scaled by its
+  router weight, is rounded to BF16 before the top-k sum, the model's dtype
+  between the expert stage and the sum as in the fused-MoE kernels the
+  model is built on (sglang-metis 0.1.0, the package description and
+  "Limitations"); the k BF16 outputs of a token are summed (exactly, in
+  float64 here) and rounded once to BF16. Router weights are inputs and are
+  not renormalised here.
 * Slots are the flat indices t*k + j. The expert-sorted order is a stable
   sort of the slots by expert id; ids outside [0, E) are dropped and
   contribute nothing.
@@ -32,11 +35,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bf16 import round_to_bf16_bits
+from .bf16 import bf16_bits_to_f64, round_to_bf16_bits
 from .linear import dequant_sum
 from .quant import quantize_rows
 
-__all__ = ["route", "grouped_gate_up", "swiglu_f32", "moe_pass", "moe_two_pass"]
+__all__ = ["route", "grouped_gate_up", "swiglu_f32", "bf16_values", "moe_pass", "moe_two_pass"]
 
 
 def route(ids, E: int):
@@ -88,6 +91,11 @@ def swiglu_f32(gu) -> np.ndarray:
     return (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
 
 
+def bf16_values(y) -> np.ndarray:
+    """float64 -> the float64 value of its nearest-even BF16."""
+    return bf16_bits_to_f64(round_to_bf16_bits(y))
+
+
 def moe_pass(qx, sx, ids, w, qw13, s13, qw2, s2, keep=False):
     """One routed-expert pass on quantised tokens.
 
@@ -116,7 +124,7 @@ def moe_pass(qx, sx, ids, w, qw13, s13, qw2, s2, keep=False):
         acc = dequant_sum(qh[lo:hi], qw2[e])
         y = (sh[lo:hi].astype(np.float64)[:, None] *
              np.asarray(s2[e], np.float32).astype(np.float64)[None, :]) * acc
-        np.add.at(out, slots // k, w[slots][:, None] * y)
+        np.add.at(out, slots // k, bf16_values(w[slots][:, None] * y))
     extra = None
     if keep:
         extra = {"gu": gu, "h": h, "qh": qh, "sh": sh, "vh": vh, "perm": perm}

@@ -30,8 +30,9 @@ quantisation and the linear layer on it:
   exact while the scaled block results span fewer than about 2**40 in
   magnitude, and otherwise off by float64 rounding only.
 * Routed experts (``moe_mxfp4_pass``): the chain of the FP8 oracle (routing,
-  W13 = [gate; up], h = fl32(silu(g) * u), router-weighted combine summed in
-  float64 and rounded once to BF16) with every expert input in MXFP4: each
+  W13 = [gate; up], h = fl32(silu(g) * u), each routed copy's weighted
+  output rounded to BF16, the k copies summed and rounded once to BF16)
+  with every expert input in MXFP4: each
   token's BF16 row quantised once over H, each routed copy's h quantised
   over I. The weights W13[e] [2I, H] and W2[e] [H, I] are MXFP4 along their
   input dimension.
@@ -41,7 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 from .bf16 import round_to_bf16_bits
-from .moe import route, swiglu_f32
+from .moe import bf16_values, route, swiglu_f32
 
 __all__ = ["E2M1_MAX", "e2m1_decode", "e2m1_encode", "mx_quantize_rows", "mx_unpack", "mx_dequant",
            "mxfp4_linear", "e8m0_value", "moe_mxfp4_pass", "moe_mxfp4_two_pass"]
@@ -164,7 +165,7 @@ def moe_mxfp4_pass(x32, ids, w, q13, s13, q2, s2, keep=False):
         slots = perm[lo:hi]
         assert np.all(flat_e[slots] == e)
         y = mxfp4_linear(qh[lo:hi], sh[lo:hi], q2[e], s2[e])[0]
-        np.add.at(out, slots // k, w[slots][:, None] * y)
+        np.add.at(out, slots // k, bf16_values(w[slots][:, None] * y))
     extra = None
     if keep:
         extra = {"qx": qx, "sx": sx, "gu": gu, "h": h, "qh": qh, "sh": sh, "perm": perm}

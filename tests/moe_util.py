@@ -62,6 +62,20 @@ def sorted_rows_gate_up(qx, sx, ids, perm, rows, q13, s13, k):
     return gu, err
 
 
+def swiglu_bound(gu64, gu_err):
+    """The oracle's h = fl32(silu(g) * u) of exact gate/up rows, and a bound dh
+    on a GPU's float32 h whose g, u are within ``gu_err``: the derivative
+    bound of silu times the error of g, the error of u, and 2**-19 relative
+    for the float32 evaluation with a fast exponential. Returns (h, dh)."""
+    I = gu64.shape[1] // 2
+    g, u = gu64[:, :I], gu64[:, I:]
+    dg, du = gu_err[:, :I], gu_err[:, I:]
+    silu = g / (1.0 + np.exp(-g))
+    h32 = oracle.swiglu_f32(gu64)
+    dh = SILU_DERIV_MAX * dg * (np.abs(u) + du) + np.abs(silu) * du + 2.0 ** -19 * np.abs(h32) + 1e-30
+    return h32, dh
+
+
 def check_requant(qh_gpu, sh_gpu, gu64, gu_err):
     """Explainable-flip check of requantised h rows against the oracle.
 
@@ -73,14 +87,8 @@ def check_requant(qh_gpu, sh_gpu, gu64, gu_err):
     equals the oracle's code unless v lies within dv of a rounding boundary.
     Returns a dict of statistics; raises AssertionError on a violation.
     """
-    I = gu64.shape[1] // 2
-    g, u = gu64[:, :I], gu64[:, I:]
-    dg, du = gu_err[:, :I], gu_err[:, I:]
-    sig = 1.0 / (1.0 + np.exp(-g))
-    silu = g * sig
-    h32 = oracle.swiglu_f32(gu64)
+    h32, dh = swiglu_bound(gu64, gu_err)
     q_ref, s_ref, v_ref = oracle.quantize_rows(h32)
-    dh = SILU_DERIV_MAX * dg * (np.abs(u) + du) + np.abs(silu) * du + 2.0 ** -19 * np.abs(h32) + 1e-30
     # scale: amax moves by at most max dh of the row
     ds = np.max(dh, axis=1) / 448.0 + 2.0 ** -22 * s_ref
     s_gpu = np.asarray(sh_gpu, np.float64)
@@ -102,8 +110,11 @@ def check_requant(qh_gpu, sh_gpu, gu64, gu_err):
 def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
     """Oracle down projection + combine for ``tokens``, from sorted h codes.
 
-    Returns (out64 [n, H], err [n, H]); err bounds |out_gpu - out64| before the
-    final BF16 rounding (E4M3 matrix-core path, float32 scaling and sums).
+    Each routed copy's output is rounded to BF16 and the copies are summed
+    exactly. Returns (out64 [n, H], err [n, H]); err bounds |out_gpu - out64|
+    before the final BF16 rounding: per copy the E4M3 matrix-core bound plus
+    one BF16 ulp (the GPU rounds its float32 value, which may sit on the other
+    side of a rounding midpoint), then the float32 sum.
     """
     tokens = np.asarray(tokens)
     E, H, I = q2.shape
@@ -126,9 +137,10 @@ def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
             b = oracle.decode(q2[e])
             scale = (sh[rows[sel]].astype(np.float64) * w[slots[sel]])[:, None] * s2[e].astype(np.float64)[None, :]
             y = scale * (a @ b.T)
-            out[sel] += y
+            ey = (MFMA_GROUP_ERR + (I / 128 + 4) * U32) * 1.01 * scale * (np.abs(a) @ np.abs(b).T)
+            out[sel] += oracle.bf16_values(y)
             absout[sel] += np.abs(y)
-            err[sel] += (MFMA_GROUP_ERR + (I / 128 + 4) * U32) * 1.01 * scale * (np.abs(a) @ np.abs(b).T)
+            err[sel] += ey + bf16_ulp(np.abs(y) + ey)
     err += (k + 2) * U32 * 1.01 * absout
     return out, err
 

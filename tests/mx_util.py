@@ -10,9 +10,8 @@ import numpy as np
 
 import oracle
 import synth
-from gpu_util import MFMA_GROUP_ERR, U32
-
-SILU_DERIV_MAX = 1.1  # max |d silu / dg| over the reals is ~1.0998
+from gpu_util import MFMA_GROUP_ERR, U32, bf16_ulp
+from moe_util import swiglu_bound
 
 
 def mx_quantize_chunked(x, rows=2048):
@@ -80,8 +79,8 @@ def check_mx_requant(qh_gpu, sh_gpu, gu64, gu_err):
     """Explainable-difference check of MXFP4 h rows against the oracle.
 
     The oracle quantises h = fl32(silu(g) * u) of its exact gate/up values.
-    The GPU's g, u lie within ``gu_err``; carried through silu * u (plus
-    float32 evaluation) that bounds the GPU's h within dh of the oracle's.
+    The GPU's g, u lie within ``gu_err``; swiglu_bound carries that to a
+    bound dh on the GPU's h.
     Then (a) a block's E8M0 byte must lie between the bytes of the block
     maxima of |h| - dh and |h| + dh, and (b) under the GPU's own block
     scale, each code must decode inside [dec(enc(v - dv)), dec(enc(v + dv))]
@@ -90,12 +89,9 @@ def check_mx_requant(qh_gpu, sh_gpu, gu64, gu_err):
     within the propagated error of a rounding or binade boundary.
     """
     I = gu64.shape[1] // 2
-    g, u = gu64[:, :I], gu64[:, I:]
-    dg, du = gu_err[:, :I], gu_err[:, I:]
-    silu = g / (1.0 + np.exp(-g))
-    h32 = oracle.swiglu_f32(gu64).astype(np.float64)
+    h32, dh = swiglu_bound(gu64, gu_err)
+    h32 = h32.astype(np.float64)
     q_ref, s_ref = oracle.mx_quantize_rows(h32.astype(np.float32))
-    dh = SILU_DERIV_MAX * dg * (np.abs(u) + du) + np.abs(silu) * du + 2.0 ** -19 * np.abs(h32) + 1e-30
     n, nb = h32.shape[0], I // 32
     hb, db = np.abs(h32).reshape(n, nb, 32), dh.reshape(n, nb, 32)
     lo_code = _block_codes(np.maximum(hb - db, 0).max(axis=2))
@@ -117,7 +113,8 @@ def check_mx_requant(qh_gpu, sh_gpu, gu64, gu_err):
 
 
 def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
-    """Exact down projection + combine for ``tokens`` from sorted MXFP4 h rows,
+    """Exact down projection + combine for ``tokens`` from sorted MXFP4 h rows
+    (each routed copy's output rounded to BF16, the copies summed exactly),
     and a bound on |out_gpu - out64| before the final BF16 rounding."""
     tokens = np.asarray(tokens)
     E, H, _ = q2.shape
@@ -141,8 +138,9 @@ def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
             b = oracle.mx_dequant(q2[e], s2[e])
             wt = w[slots[sel]][:, None]
             y = wt * (a @ b.T)
-            out[sel] += y
+            ey = np.abs(wt) * mx_bound(a, b, I)
+            out[sel] += oracle.bf16_values(y)
             absout[sel] += np.abs(y)
-            err[sel] += np.abs(wt) * mx_bound(a, b, I)
+            err[sel] += ey + bf16_ulp(np.abs(y) + ey)
     err += (k + 2) * U32 * 1.01 * absout
     return out, err

@@ -4,7 +4,8 @@
   expert in increasing slot order; a loop-by-loop construction on small
   inputs gives the same arrays; out-of-range ids are dropped.
 * One expert, top-1, weight 1 reduces to two dense layers with SwiGLU and a
-  requantisation between them, computed with the dense oracle.
+  requantisation between them, computed with the dense oracle; the output
+  is the second layer's BF16 output.
 * k routed copies of one expert whose weights sum to 1 give that expert's
   output; relabelling experts (ids and weight stacks together) and
   reordering tokens act as they must.
@@ -76,7 +77,7 @@ def test_single_expert_reduces_to_dense_chain():
     y, ybf = oracle.w8a8_linear(qh, sh, d["q2"][0], d["s2"][0])
     assert np.array_equal(extra["perm"], np.arange(T))
     assert np.array_equal(extra["qh"], qh) and np.array_equal(extra["sh"], sh)
-    assert np.array_equal(out64, y) and np.array_equal(out_bf, ybf)
+    assert np.array_equal(out64, oracle.bf16_bits_to_f64(ybf)) and np.array_equal(out_bf, ybf)
 
 
 def test_k_copies_of_one_expert_weights_summing_to_one():
@@ -90,11 +91,12 @@ def test_k_copies_of_one_expert_weights_summing_to_one():
     w2 = np.full((T, 2), 0.5, np.float32)
     out, out_bf, _ = oracle.moe_pass(d["qx"], d["sx"], ids2, w2, d["q13"], d["s13"], d["q2"], d["s2"])
     assert np.array_equal(out, base) and np.array_equal(out_bf, base_bf)
-    # four copies: equal up to float64 rounding of the sum
+    # four copies with power-of-two weights: each BF16 copy is an exact
+    # fraction of the single copy, so the sum is exact too
     ids4 = np.full((T, 4), 2, np.int32)
     w4 = np.tile(np.array([0.5, 0.25, 0.125, 0.125], np.float32), (T, 1))
     out4, _, _ = oracle.moe_pass(d["qx"], d["sx"], ids4, w4, d["q13"], d["s13"], d["q2"], d["s2"])
-    assert np.allclose(out4, base, rtol=1e-15, atol=0)
+    assert np.array_equal(out4, base)
 
 
 def test_relabelled_experts_and_reordered_tokens():
@@ -106,9 +108,8 @@ def test_relabelled_experts_and_reordered_tokens():
     inv = np.argsort(relabel)                                      # new id -> old id
     out2, _, _ = oracle.moe_pass(d["qx"], d["sx"], relabel[d["ids"]], d["w"],
                                  d["q13"][inv], d["s13"][inv], d["q2"][inv], d["s2"][inv])
-    # the k terms of a token are summed in another order: float64 rounding only
-    tol = 1e-14 * np.abs(out).max()
-    assert np.allclose(out2, out, rtol=0, atol=tol)
+    # the k BF16 terms of a token are summed in another order: exact in float64
+    assert np.array_equal(out2, out)
     order = np.random.default_rng(6).permutation(d["qx"].shape[0])
     out3, _, _ = oracle.moe_pass(d["qx"][order], d["sx"][order], d["ids"][order], d["w"][order], *args)
     assert np.array_equal(out3, out[order])
@@ -125,7 +126,7 @@ def test_dropped_ids_contribute_nothing():
     w0[::2, 0] = 0.0
     ids0 = d["ids"].copy()
     ref, _, _ = oracle.moe_pass(d["qx"], d["sx"], ids0, w0, *args)
-    assert np.allclose(out, ref, rtol=1e-14, atol=1e-300)
+    assert np.array_equal(out, ref)
 
 
 def test_silu_matches_torch():

@@ -358,7 +358,7 @@ def moe_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_sca
                      y=None):
     """Down projection of the sorted rows and the router-weighted combine: BF16 [T, H].
 
-    perm/offsets come from ``moe_route(..., order=order)``; ``y`` is float32
+    perm/offsets come from ``moe_route(..., order=order)``; ``y`` is BF16
     scratch [T*k, H] for the per-slot products."""
     import torch
 
@@ -371,9 +371,9 @@ def moe_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_sca
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
     if y is None:
-        y = torch.empty((T * k, H), dtype=torch.float32, device=h_q.device)
-    if y.numel() < T * k * H or y.dtype != torch.float32:
-        raise ValueError("y must be float32 with at least T * k * H elements")
+        y = torch.empty((T * k, H), dtype=torch.bfloat16, device=h_q.device)
+    if y.numel() < T * k * H or y.dtype != torch.bfloat16:
+        raise ValueError("y must be bfloat16 with at least T * k * H elements")
     _check("moe_down_combine", lib().moe_down_combine(
         h_q.data_ptr(), h_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), topk_ids.data_ptr(),
         topk_w.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), y.data_ptr(), T, H, I, E, k,
@@ -560,9 +560,9 @@ def moe_mxfp4_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, 
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
     if y is None:
-        y = torch.empty((T * k, H), dtype=torch.float32, device=h_q.device)
-    if y.numel() < T * k * H or y.dtype != torch.float32:
-        raise ValueError("y must be float32 with at least T * k * H elements")
+        y = torch.empty((T * k, H), dtype=torch.bfloat16, device=h_q.device)
+    if y.numel() < T * k * H or y.dtype != torch.bfloat16:
+        raise ValueError("y must be bfloat16 with at least T * k * H elements")
     oq = os_ = None
     if quantize_output:
         oq = torch.empty((T, H // 2), dtype=torch.uint8, device=h_q.device)

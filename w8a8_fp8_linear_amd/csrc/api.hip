@@ -266,21 +266,21 @@ int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int
 
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
                      const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const float* w2_scale,
-                     uint16_t* out_bf16, float* y_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     uint16_t* out_bf16, uint16_t* y_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                      int order, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
   if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (!mul_ok(T * topk, H) || !mul_ok(T * topk * H, 4)) return W8A8_ERR_BAD_SHAPE;
   if (T == 0) return W8A8_OK;
-  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
+  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16}))
     return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16}))
     return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
-                                                 out_bf16, y_f32, nullptr, nullptr, T, H, I, E, topk, order, stream));
+                                                 out_bf16, y_bf16, nullptr, nullptr, T, H, I, E, topk, order, stream));
 }
 
 size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -397,20 +397,20 @@ int moe_mxfp4_gate_up_swiglu_quant(const uint8_t* x_q, const uint8_t* x_scale, c
 
 int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int32_t* perm, const int32_t* offsets,
                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const uint8_t* w2_scale,
-                           uint16_t* out_bf16, float* y_f32, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
+                           uint16_t* out_bf16, uint16_t* y_bf16, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
                            int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
   const int c = check_mx_moe(T, H, I, E, topk, order);
   if (c != W8A8_OK) return c;
   if (T == 0) return W8A8_OK;
-  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
+  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16}))
     return W8A8_ERR_NULL_ARG;
   if ((out_q == nullptr) != (out_scale == nullptr)) return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32, out_q, out_scale}))
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16, out_q, out_scale}))
     return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_mx_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
-                                                    out_bf16, y_f32, out_q, out_scale, T, H, I, E, topk, order,
+                                                    out_bf16, y_bf16, out_q, out_scale, T, H, I, E, topk, order,
                                                     stream));
 }
 

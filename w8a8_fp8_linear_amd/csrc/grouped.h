@@ -1,6 +1,6 @@
 // Device helpers shared by the grouped (routed-expert) kernels of both
 // expert formats: the tile lookup over the device-side group offsets and the
-// ordered per-token sum of the slot rows.
+// ordered per-token sum of the BF16 slot rows.
 #pragma once
 
 #include "device.h"
@@ -47,18 +47,17 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
   return false;
 }
 
-// Sum of a token's valid slot rows at columns c0 .. c0 + 7, in the order
-// j = 0, 1, ... in float32 (deterministic). The k rows of a token are
-// contiguous in y; they are loaded (non-temporal: each byte is read once;
-// measured 8% faster on this stage) before any is added, and a dropped
-// slot's row is read but not used.
-__device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __restrict__ ids, int64_t t, int topk,
-                                  int Eids, int H, int c0, float4& a, float4& b) {
+// Sum of a token's valid BF16 slot rows at columns c0 .. c0 + 7, in the
+// order j = 0, 1, ... in float32 (deterministic). The k rows of a token are
+// contiguous in y; they are loaded (non-temporal: each byte is read once)
+// before any is added, and a dropped slot's row is read but not used.
+__device__ inline void sum_slots8(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids, int64_t t,
+                                  int topk, int Eids, int H, int c0, float4& a, float4& b) {
   a = make_float4(0.f, 0.f, 0.f, 0.f);
   b = a;
   constexpr int kBatch = 8;
   for (int j0 = 0; j0 < topk; j0 += kBatch) {
-    float4 u[kBatch], v[kBatch];
+    v4i u[kBatch];
     bool ok[kBatch];
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
@@ -66,16 +65,14 @@ __device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __
       const int64_t slot = t * topk + (j < topk ? j : 0);
       const int id = ids[slot];
       ok[jj] = j < topk && id >= 0 && id < Eids;
-      const v4f* src = reinterpret_cast<const v4f*>(y + slot * H + c0);
-      const v4f t0 = __builtin_nontemporal_load(src), t1 = __builtin_nontemporal_load(src + 1);
-      u[jj] = make_float4(t0[0], t0[1], t0[2], t0[3]);
-      v[jj] = make_float4(t1[0], t1[1], t1[2], t1[3]);
+      u[jj] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(y + slot * H + c0));
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
       if (!ok[jj]) continue;
-      a.x += u[jj].x; a.y += u[jj].y; a.z += u[jj].z; a.w += u[jj].w;
-      b.x += v[jj].x; b.y += v[jj].y; b.z += v[jj].z; b.w += v[jj].w;
+      const uint32_t w0 = (uint32_t)u[jj].x, w1 = (uint32_t)u[jj].y, w2 = (uint32_t)u[jj].z, w3 = (uint32_t)u[jj].w;
+      a.x += bf16_lo(w0); a.y += bf16_hi(w0); a.z += bf16_lo(w1); a.w += bf16_hi(w1);
+      b.x += bf16_lo(w2); b.y += bf16_hi(w2); b.z += bf16_lo(w3); b.w += bf16_hi(w3);
     }
   }
 }

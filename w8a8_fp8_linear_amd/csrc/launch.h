@@ -56,12 +56,12 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
                                        int64_t I, int64_t E, int64_t topk, int order, void* ws,
                                        hipStream_t stream);
 
-// y: [T*topk, H] float32 scratch (down_combine_scratch_bytes).
+// y: [T*topk, H] BF16 scratch (down_combine_scratch_bytes).
 size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk);
 // out_q / out_s (both NULL or both set): also quantize_per_token(out).
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
                                const int32_t* offsets, const int32_t* ids, const float* tw,
-                               const uint8_t* w2, const float* s2, uint16_t* out, float* y,
+                               const uint8_t* w2, const float* s2, uint16_t* out, uint16_t* y,
                                uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I,
                                int64_t E, int64_t topk, int order, hipStream_t stream);
 
@@ -89,11 +89,11 @@ hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, 
                                           const uint8_t* s13, uint8_t* qh, uint8_t* sh, int64_t T, int64_t H,
                                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
-// y: [T*topk, H] float32 scratch; out_q / out_s (both NULL or both set): also
+// y: [T*topk, H] BF16 scratch; out_q / out_s (both NULL or both set): also
 // the MXFP4 quantisation of out.
 hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
-                                  uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
+                                  uint16_t* out, uint16_t* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
                                   int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
 size_t mx_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);

@@ -10,8 +10,10 @@
 // onto SGLang"). The expert activation, the gate/up layout, the requantised
 // expert input and the combine are not printed; the readings taken are:
 // W13[e] = [gate; up] rows, h = silu(g) * u in float32, one E4M3 scale per
-// routed copy (slot) of h, out[t] = bf16(sum_j w[t,j] * y[t,j]) with float32
-// sums.
+// routed copy (slot) of h, each routed copy's weighted output rounded to
+// BF16 (the model's dtype between the expert stage and the top-k sum, as in
+// the fused-MoE kernels the model is built on: sglang-metis 0.1.0, the
+// package description), out[t] = bf16(sum_j y[t,j]) with float32 sums.
 //
 // Kernels
 //  * route_count / route_scatter: slots t*k+j are grouped by expert (or by
@@ -34,10 +36,11 @@
 //      DOWN_Y     A = the requantised rows (sorted, contiguous), B = W2 of
 //                 the tile's expert; the epilogue applies the row scale, the
 //                 channel scale and the router weight and stores the slot's
-//                 float32 product y to its own row.
+//                 BF16 product y to its own row.
 //  * requant_rows: elementwise E4M3 requantisation of h once the row maxima
 //    are known (scale = amax / 448, correctly rounded division, RNE).
-//  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots, added
+//  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots (BF16
+//    rows, float32 sums), added
 //    in the fixed order j = 0, 1, ... (deterministic, no atomics; float32
 //    atomics measured ~3x slower than this whole stage). The k rows of a
 //    token are contiguous, so this is one streaming pass. combine_quant also
@@ -227,8 +230,8 @@ struct GroupedArgs {
   const uint8_t* B;         // [E, N, K] weight codes
   const float* sB;          // [E, N] weight row scales
   const float* tw;          // DOWN_Y: router weights [slots]
-  uint16_t* out_bf16;       // GATE_UP: [rows, N]
-  float* out_f32;           // GATE_UP_H: h [rows, N / 2]; DOWN_Y: y [slots, N]
+  uint16_t* out_bf16;       // GATE_UP: [rows, N]; DOWN_Y: y [slots, N]
+  float* out_f32;           // GATE_UP_H: h [rows, N / 2]
   uint32_t* row_amax;       // GATE_UP_H: max |h| bits per output row (cleared by the caller)
   const int32_t* dst_row;   // GATE_UP_H: slot -> output row (NULL: the sorted row itself)
   int N, K, tiles_n, tiles_m_max;
@@ -249,9 +252,9 @@ struct GroupedArgs {
 //             partial max |h| with an integer atomicMax on the float bits
 //             (order-independent, so the row maximum is exact).
 //  DOWN_Y:    A row = h codes of sorted row r (contiguous); the epilogue
-//             stores w[slot] * sA[r] * sB[e, n] * acc to row `slot` of
-//             out_f32 [T * topk, N] straight from registers, a lane owning 4
-//             consecutive columns of a row (every slot is written once).
+//             stores bf16(w[slot] * sA[r] * sB[e, n] * acc) to row `slot` of
+//             out_bf16 [T * topk, N] straight from registers, a lane owning
+//             4 consecutive columns of a row (every slot is written once).
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
@@ -384,15 +387,16 @@ void grouped_tiled(const GroupedArgs p) {
       const int slot = row_tok[ml];
       if (slot < 0) continue;
       const float s = row_scale[ml];
-      float* yrow = p.out_f32 + (int64_t)slot * N;
+      uint16_t* yrow = p.out_bf16 + (int64_t)slot * N;
 #pragma unroll
       for (int i = 0; i < C::SN; ++i) {
         const int n = n0 + wn * C::WN + i * 16 + 4 * g;
         if (n >= N) continue;
         const float4 sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n);
         const v4f a = acc[i][j];
-        *reinterpret_cast<float4*>(yrow + n) =
-            make_float4(a[0] * s * sW.x, a[1] * s * sW.y, a[2] * s * sW.z, a[3] * s * sW.w);
+        *reinterpret_cast<uint2*>(yrow + n) =
+            make_uint2(f32_to_bf16_rne(a[0] * s * sW.x) | (f32_to_bf16_rne(a[1] * s * sW.y) << 16),
+                       f32_to_bf16_rne(a[2] * s * sW.z) | (f32_to_bf16_rne(a[3] * s * sW.w) << 16));
       }
     }
     return;
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, i
 
 // out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots.
 // One thread per 8 columns.
-__global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void combine_slots(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
                                                      int64_t T, int topk, int Eids, int H,
                                                      uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -537,7 +541,7 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
 // makes of out[t]: amax on the BF16 bits, s = fl32(amax / 448), codes of
 // fl32(x / s) (the same shared quantiser code).
 template <int PER>
-__global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void combine_quant(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
                                                      int topk, int Eids, int H, uint16_t* __restrict__ out,
                                                      uint8_t* __restrict__ q, float* __restrict__ qs) {
   __shared__ uint32_t wmax[4];
@@ -691,7 +695,7 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
 // to its own row of y), then the per-token combine.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm, const int32_t* offsets,
                                const int32_t* ids, const float* tw, const uint8_t* w2, const float* s2, uint16_t* out,
-                               float* y, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I, int64_t E,
+                               uint16_t* y, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I, int64_t E,
                                int64_t topk, int order, hipStream_t stream) {
   GroupedArgs a{};
   a.A = qh;
@@ -705,7 +709,7 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   a.B = w2;
   a.sB = s2;
   a.tw = tw;
-  a.out_f32 = y;
+  a.out_bf16 = y;
   a.N = (int)H;
   a.K = (int)I;
   const hipError_t err = run_grouped_auto<kDownY>(a, T * topk, T * topk / a.G, stream);
@@ -729,12 +733,12 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   return launch_quantize_rows(out, T, H, out_q, out_s, stream);
 }
 
-size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk) { return (size_t)(T * topk * H * 4); }
+size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk) { return (size_t)(T * topk * H * 2); }
 
 // Workspace of the full pass:
 //   counts | offsets | perm | route scratch | qh | sh | amax | big
 // where big holds h [T*k, I] float32 during the gate/up and then the
-// weighted slot products y [T*k, H] float32 of the down projection.
+// weighted slot products y [T*k, H] BF16 of the down projection.
 struct MoeLayout {
   int64_t counts, offsets, perm, route, qh, sh, amax, big, total;
 };
@@ -750,7 +754,7 @@ static MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t 
   L.qh = o; o += align256(n * I);
   L.sh = o; o += align256(n * 4);
   L.amax = o; o += align256(n * 4);  // amax | big is the gate/up stage's workspace
-  L.big = o; o += std::max(align256(n * I * 4), align256(n * H * 4));
+  L.big = o; o += std::max(align256(n * I * 4), align256(n * H * 2));
   L.total = o;
   return L;
 }
@@ -777,7 +781,7 @@ hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, co
   err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, T, H, I, E, topk, 0,
                                     b + L.amax, stream);
   if (err != hipSuccess) return err;
-  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<float*>(b + L.big), out_q,
+  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<uint16_t*>(b + L.big), out_q,
                              out_s, T, H, I, E, topk, 0, stream);
 }
 

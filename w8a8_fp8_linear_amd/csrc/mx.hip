@@ -29,13 +29,13 @@
 //    core and the epilogue has no per-row scale.
 //      GATE_UP    BF16 gate/up output in sorted order;
 //      GATE_UP_Q  gate and up weight blocks interleaved as in the FP8
-//                 kernel; the epilogue forms h = silu(g) * u, and each
-//                 wave's 32 h columns of a row are exactly one MX block, so
+//                 kernel; the epilogue forms h = silu(g) * u in float32, and
+//                 each wave's 32 h columns of a row are one MX block, so
 //                 the block maximum (a shuffle over the 4 lanes holding the
 //                 block), the exponent and the E2M1 codes are made in
 //                 registers and stored: no float32 h round trip, no row
 //                 maximum, no atomics, no second kernel;
-//      DOWN_Y     per-slot float32 y = w[slot] * acc to the slot's own row.
+//      DOWN_Y     per-slot BF16 y = bf16(w[slot] * acc) to the slot's own row.
 //  * combine_mx: the ordered per-token slot sum of the FP8 combine, with the
 //    BF16 result optionally quantised to MXFP4 in the same pass (the next
 //    pass's expert input).
@@ -165,8 +165,7 @@ struct MxArgs {
   const uint8_t* B;         // [E, N, K/2] weight codes
   const uint8_t* sB;        // [E, N, K/32] weight scales
   const float* tw;          // DOWN_Y: router weights [slots]
-  uint16_t* out_bf16;       // GATE_UP: [rows, N]
-  float* out_f32;           // DOWN_Y: y [slots, N]
+  uint16_t* out_bf16;       // GATE_UP: [rows, N]; DOWN_Y: y [slots, N]
   uint8_t* out_q;           // GATE_UP_Q: h codes [rows, N/4]
   uint8_t* out_s;           // GATE_UP_Q: h scales [rows, N/64]
   const int32_t* dst_row;   // GATE_UP_Q: slot -> output row (NULL: the sorted row)
@@ -340,13 +339,14 @@ void mx_grouped(const MxArgs p) {
       const int slot = row_tok[ml];
       if (slot < 0) continue;
       const float w = row_w[ml];
-      float* yrow = p.out_f32 + (int64_t)slot * N;
+      uint16_t* yrow = p.out_bf16 + (int64_t)slot * N;
 #pragma unroll
       for (int i = 0; i < C::SN; ++i) {
         const int n = n0 + wn * C::WN + i * 16 + 4 * g;
         if (n >= N) continue;
         const v4f a = acc[i][j];
-        *reinterpret_cast<float4*>(yrow + n) = make_float4(a[0] * w, a[1] * w, a[2] * w, a[3] * w);
+        *reinterpret_cast<uint2*>(yrow + n) = make_uint2(f32_to_bf16_rne(a[0] * w) | (f32_to_bf16_rne(a[1] * w) << 16),
+                                                         f32_to_bf16_rne(a[2] * w) | (f32_to_bf16_rne(a[3] * w) << 16));
       }
     }
     return;
@@ -423,7 +423,7 @@ void mx_grouped(const MxArgs p) {
 // the BF16 row (exactly what mx_quant_bf16 makes of it). One thread per 8
 // columns; H % 32 == 0, so a block's four threads form an aligned quad.
 template <bool QUANT>
-__global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void combine_mx(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
                                                   int64_t T, int topk, int Eids, int H, uint16_t* __restrict__ out,
                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -512,7 +512,7 @@ hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, 
 
 hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
-                                  uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
+                                  uint16_t* out, uint16_t* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
                                   int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
   MxArgs a{};
   a.A = qh;
@@ -526,7 +526,7 @@ hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const in
   a.B = w2;
   a.sB = s2;
   a.tw = tw;
-  a.out_f32 = y;
+  a.out_bf16 = y;
   a.N = (int)H;
   a.K = (int)I;
   const hipError_t err = run_mx_auto<kMxDownY>(a, T * topk, T * topk / a.G, stream);
@@ -543,7 +543,7 @@ hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const in
 }
 
 // Workspace of the full pass: counts | offsets | perm | route scratch |
-// h codes [T*k, I/2] | h scales [T*k, I/32] | y [T*k, H] float32.
+// h codes [T*k, I/2] | h scales [T*k, I/32] | y [T*k, H] BF16.
 struct MxLayout {
   int64_t counts, offsets, perm, route, qh, sh, y, total;
 };
@@ -559,7 +559,7 @@ static MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t to
   L.route = o; o += (int64_t)route_workspace_bytes(T, topk, E);
   L.qh = o; o += al(n * I / 2);
   L.sh = o; o += al(n * I / 32);
-  L.y = o; o += al(n * H * 4);
+  L.y = o; o += al(n * H * 2);
   L.total = o;
   return L;
 }
@@ -583,7 +583,7 @@ hipError_t launch_mx_moe(const uint8_t* xq, const uint8_t* xs, const int32_t* id
                                        0, stream);
   if (err != hipSuccess) return err;
   return launch_mx_down_combine(b + L.qh, b + L.sh, perm, offsets, ids, tw, w2, s2, out,
-                                reinterpret_cast<float*>(b + L.y), out_q, out_s, T, H, I, E, topk, 0, stream);
+                                reinterpret_cast<uint16_t*>(b + L.y), out_q, out_s, T, H, I, E, topk, 0, stream);
 }
 
 }  // namespace w8a8
