@@ -35,7 +35,8 @@
 //                 block), the exponent and the E2M1 codes are made in
 //                 registers and stored: no float32 h round trip, no row
 //                 maximum, no atomics, no second kernel;
-//      DOWN_Y     per-slot BF16 y = bf16(w[slot] * acc) to the slot's own row.
+//      DOWN_Y     per-slot BF16 y = bf16(w[slot] * acc), staged in LDS and
+//                 stored as whole row segments of the slot's own row.
 //  * combine_mx: the ordered per-token slot sum of the FP8 combine, with the
 //    BF16 result optionally quantised to MXFP4 in the same pass (the next
 //    pass's expert input).
@@ -144,8 +145,8 @@ struct MxTile {
   static constexpr int kLoadsB = BN / kRowsPerPass, kLoadsA = BM / kRowsPerPass;
   static constexpr int kScaleDw = kRows * 2;           // scale dwords per stage
   static constexpr int kScaleLoads = (kScaleDw + kThreads - 1) / kThreads;
-  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP only)
-  static constexpr int kEpi = MODE == kMxGateUp ? BM * kEpiStride : 0;
+  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP, DOWN_Y)
+  static constexpr int kEpi = (MODE == kMxGateUp || MODE == kMxDownY) ? BM * kEpiStride : 0;
   static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
   static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
   static_assert(kRowsPerPass % 8 == 0, "the loader's chunk swizzle needs 8-row passes");
@@ -333,21 +334,28 @@ void mx_grouped(const MxArgs p) {
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
   if (MODE == kMxDownY) {
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < C::SM; ++j) {
-      const int ml = wm * C::WM + j * 16 + r16;
-      const int slot = row_tok[ml];
-      if (slot < 0) continue;
-      const float w = row_w[ml];
-      uint16_t* yrow = p.out_bf16 + (int64_t)slot * N;
+    for (int i = 0; i < C::SN; ++i) {
+      const int nl = wn * C::WN + i * 16 + 4 * g;
 #pragma unroll
-      for (int i = 0; i < C::SN; ++i) {
-        const int n = n0 + wn * C::WN + i * 16 + 4 * g;
-        if (n >= N) continue;
+      for (int j = 0; j < C::SM; ++j) {
+        const int ml = wm * C::WM + j * 16 + r16;
+        const float w = row_w[ml];
         const v4f a = acc[i][j];
-        *reinterpret_cast<uint2*>(yrow + n) = make_uint2(f32_to_bf16_rne(a[0] * w) | (f32_to_bf16_rne(a[1] * w) << 16),
-                                                         f32_to_bf16_rne(a[2] * w) | (f32_to_bf16_rne(a[3] * w) << 16));
+        *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) =
+            make_uint2(f32_to_bf16_rne(a[0] * w) | (f32_to_bf16_rne(a[1] * w) << 16),
+                       f32_to_bf16_rne(a[2] * w) | (f32_to_bf16_rne(a[3] * w) << 16));
       }
+    }
+    __syncthreads();
+    constexpr int kRowChunks = BN / 8;
+    for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
+      const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
+      const int slot = row_tok[row];
+      if (slot >= 0 && n0 + col < N)
+        *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)slot * N + n0 + col) =
+            *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
     }
     return;
   }
