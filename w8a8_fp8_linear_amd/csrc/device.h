@@ -47,11 +47,15 @@ __device__ inline v4f mfma_16x16x128_e4m3(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// float32 -> BF16 bits, round to nearest even (finite inputs).
-__device__ inline uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two float32 -> two BF16 bit patterns (a in the low half), round to nearest
+// even, with the gfx950 packed conversion (v_cvt_pk_bf16_f32): one
+// instruction per pair. On the GPU it was compared with the integer rule
+// (u + 0x7FFF + ((u >> 16) & 1)) >> 16 on every non-NaN float32 bit pattern:
+// 0 mismatches; NaN stays NaN.
+__device__ inline uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -149,11 +149,9 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
       const v4f a = acc[i][j];
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * sA[j] * sW.x);
-      const uint32_t b1 = f32_to_bf16_rne(a[1] * sA[j] * sW.y);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * sA[j] * sW.z);
-      const uint32_t b3 = f32_to_bf16_rne(a[3] * sA[j] * sW.w);
-      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0] * sA[j] * sW.x, a[1] * sA[j] * sW.y);
+      const uint32_t p1 = bf16x2_rne(a[2] * sA[j] * sW.z, a[3] * sA[j] * sW.w);
+      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(p0, p1);
     }
   }
   __syncthreads();
@@ -228,11 +226,9 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
     const int m = t * 16 + r16;
     if (m < M) {
       const float s = sa[m];
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * s * sW.x);
-      const uint32_t b1 = f32_to_bf16_rne(a[1] * s * sW.y);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * s * sW.z);
-      const uint32_t b3 = f32_to_bf16_rne(a[3] * s * sW.w);
-      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0] * s * sW.x, a[1] * s * sW.y);
+      const uint32_t p1 = bf16x2_rne(a[2] * s * sW.z, a[3] * s * sW.w);
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
     }
   }
 }
@@ -328,11 +324,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict_
     const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
     const int m = t * 16 + r16;
     if (m < M) {
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * s[t] * sW.x);
-      const uint32_t b1 = f32_to_bf16_rne(a[1] * s[t] * sW.y);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * s[t] * sW.z);
-      const uint32_t b3 = f32_to_bf16_rne(a[3] * s[t] * sW.w);
-      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0] * s[t] * sW.x, a[1] * s[t] * sW.y);
+      const uint32_t p1 = bf16x2_rne(a[2] * s[t] * sW.z, a[3] * s[t] * sW.w);
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
     }
   }
 }

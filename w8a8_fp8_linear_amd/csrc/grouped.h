@@ -78,8 +78,7 @@ __device__ inline void sum_slots8(const uint16_t* __restrict__ y, const int32_t*
 }
 
 __device__ inline uint4 to_bf16x8(float4 a, float4 b) {
-  return make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16), f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
-                    f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16), f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
+  return make_uint4(bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y), bf16x2_rne(b.z, b.w));
 }
 
 }  // namespace w8a8

@@ -397,8 +397,8 @@ void grouped_tiled(const GroupedArgs p) {
         const float s = row_scale[ml];
         const v4f a = acc[i][j];
         *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) =
-            make_uint2(f32_to_bf16_rne(a[0] * s * sW.x) | (f32_to_bf16_rne(a[1] * s * sW.y) << 16),
-                       f32_to_bf16_rne(a[2] * s * sW.z) | (f32_to_bf16_rne(a[3] * s * sW.w) << 16));
+            make_uint2(bf16x2_rne(a[0] * s * sW.x, a[1] * s * sW.y),
+                       bf16x2_rne(a[2] * s * sW.z, a[3] * s * sW.w));
       }
     }
     __syncthreads();
@@ -467,9 +467,9 @@ void grouped_tiled(const GroupedArgs p) {
       const int ml = wm * C::WM + j * 16 + r16;
       const float s = row_scale[ml];
       const v4f a = acc[i][j];
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * s * sW.x), b1 = f32_to_bf16_rne(a[1] * s * sW.y);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * s * sW.z), b3 = f32_to_bf16_rne(a[3] * s * sW.w);
-      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0] * s * sW.x, a[1] * s * sW.y);
+      const uint32_t p1 = bf16x2_rne(a[2] * s * sW.z, a[3] * s * sW.w);
+      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(p0, p1);
     }
   }
   __syncthreads();

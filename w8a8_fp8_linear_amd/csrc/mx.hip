@@ -344,8 +344,8 @@ void mx_grouped(const MxArgs p) {
         const float w = row_w[ml];
         const v4f a = acc[i][j];
         *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) =
-            make_uint2(f32_to_bf16_rne(a[0] * w) | (f32_to_bf16_rne(a[1] * w) << 16),
-                       f32_to_bf16_rne(a[2] * w) | (f32_to_bf16_rne(a[3] * w) << 16));
+            make_uint2(bf16x2_rne(a[0] * w, a[1] * w),
+                       bf16x2_rne(a[2] * w, a[3] * w));
       }
     }
     __syncthreads();
@@ -411,9 +411,9 @@ void mx_grouped(const MxArgs p) {
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
       const v4f a = acc[i][j];
-      const uint32_t b0 = f32_to_bf16_rne(a[0]), b1 = f32_to_bf16_rne(a[1]);
-      const uint32_t b2 = f32_to_bf16_rne(a[2]), b3 = f32_to_bf16_rne(a[3]);
-      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0], a[1]);
+      const uint32_t p1 = bf16x2_rne(a[2], a[3]);
+      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(p0, p1);
     }
   }
   __syncthreads();

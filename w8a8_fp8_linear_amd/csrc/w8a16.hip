@@ -173,9 +173,9 @@ void w8a16_tiled(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W, 
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
       const v4f a = acc[i][j];
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * s.x), b1 = f32_to_bf16_rne(a[1] * s.y);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * s.z), b3 = f32_to_bf16_rne(a[3] * s.w);
-      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0] * s.x, a[1] * s.y);
+      const uint32_t p1 = bf16x2_rne(a[2] * s.z, a[3] * s.w);
+      *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) = make_uint2(p0, p1);
     }
   }
   __syncthreads();
@@ -248,9 +248,9 @@ __global__ __launch_bounds__(256) void w8a16_skinny(const uint16_t* __restrict__
     const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
     const int m = t * 16 + r16;
     if (m < M) {
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * s.x), b1 = f32_to_bf16_rne(a[1] * s.y);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * s.z), b3 = f32_to_bf16_rne(a[3] * s.w);
-      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const uint32_t p0 = bf16x2_rne(a[0] * s.x, a[1] * s.y);
+      const uint32_t p1 = bf16x2_rne(a[2] * s.z, a[3] * s.w);
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
     }
   }
 }
