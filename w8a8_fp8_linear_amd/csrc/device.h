@@ -58,6 +58,12 @@ __device__ inline uint32_t bf16x2_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// silu(g) = g / (1 + e^-g) in float32 with the hardware exponential and
+// reciprocal (each within about 1 ulp): a few instructions instead of a
+// correctly rounded division. The result stays within a few float32 ulps of
+// the exact value (e^-g overflowing to infinity gives -0).
+__device__ inline float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

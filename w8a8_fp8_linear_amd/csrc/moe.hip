@@ -438,7 +438,7 @@ void grouped_tiled(const GroupedArgs p) {
         for (int r = 0; r < 4; ++r) {
           const float gv = ga[r] * rs[j] * gs[r];
           const float uv = ua[r] * rs[j] * us[r];
-          h[r] = gv / (1.0f + __expf(-gv)) * uv;
+          h[r] = silu_f32(gv) * uv;
           amax[j] = fmaxf(amax[j], fabsf(h[r]));
         }
         if (dsts[j] >= 0)

@@ -377,7 +377,7 @@ void mx_grouped(const MxArgs p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float gv = ga[r], uv = ua[r];
-            const float hv = gv / (1.0f + __expf(-gv)) * uv;
+            const float hv = silu_f32(gv) * uv;
             h[4 * half + r] = hv;
             amax = fmaxf(amax, fabsf(hv));
           }
