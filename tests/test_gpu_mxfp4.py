@@ -12,7 +12,9 @@
   output and the oracle's quantiser, bit for bit.
 * Full pass: normalised Frobenius <= 4e-3 against the oracle, on small and
   ragged shapes, the pages' expert shapes and the two-pass stack (pass 2
-  teacher-forced).
+  teacher-forced); edge shapes (one token and one expert, H = I = 128,
+  H = 8192, I = 2048, a zero token row) and 1024 routing groups in the
+  slot-position order.
 """
 import numpy as np
 import pytest
@@ -310,3 +312,65 @@ def test_all_slots_dropped_gives_zeros(small):
                                dv["s13"], dv["q2"], dv["s2"])
     torch.cuda.synchronize()
     assert not bf16_bits(out).any()
+
+
+@pytest.mark.parametrize("cfg", [dict(T=1, H=128, I=128, E=1, k=1), dict(T=3, H=128, I=128, E=2, k=2),
+                                 dict(T=70, H=8192, I=128, E=3, k=2), dict(T=40, H=128, I=2048, E=4, k=3)])
+def test_edge_shapes_full_pass(cfg):
+    """One token and one expert; the smallest sizes (H = I = 128); a wide latent
+    (H = 8192: 32 K steps in the gate/up, 32 output tiles in the down
+    projection); a wide intermediate (I = 2048). A zero token row is included
+    where there is more than one token. Full pass against the oracle, and the
+    fused MXFP4 output quantisation bit-exact against the oracle's quantiser."""
+    print(f"[mx edge] {cfg}", flush=True)
+    d = quantized_mx_moe(**cfg, n_outlier=1, seed=31)
+    if cfg["T"] > 1:
+        d["x_bits"] = d["x_bits"].copy()
+        d["x_bits"][0] = 0
+        d["x32"] = oracle.bf16_bits_to_f64(d["x_bits"]).astype(np.float32)
+        d["qx"], d["sx"] = oracle.mx_quantize_rows(d["x32"])
+    dv = _dev(d)
+    ids, w = d["routes"][0]
+    out, q, s = w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"],
+                                     dv["s2"], quantize_output=True)
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    rep = bf16_compare(got, _oracle_tokens(d["x32"], ids, w, d, np.arange(d["T"])))
+    record(f"mxfp4 edge shape T={cfg['T']} H={cfg['H']} I={cfg['I']} E={cfg['E']} k={cfg['k']}", rep)
+    assert rep["frobenius"] <= 4e-3, rep
+    if cfg["T"] > 1:
+        assert not got[0].any()
+    qo, so = oracle.mx_quantize_rows(oracle.bf16_bits_to_f64(got).astype(np.float32))
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(s.cpu().numpy(), so)
+
+
+def test_slot_position_order_with_1024_groups():
+    """Order 1 with top-16 of 64 experts: 1024 routing groups, most of them tiny,
+    through the fused gate/up and the down projection."""
+    d = quantized_mx_moe(T=200, H=256, I=128, E=64, k=16, n_outlier=1, seed=37)
+    hq, hs, perm, offsets = _check_fused(d, tile_order=1, row_order=1)
+    _check_down(d, hq, hs, perm, offsets, order=1)
+
+
+def test_mxfp4_argument_errors(small):
+    dv = _dev(small)
+    T, k = small["T"], small["k"]
+    ids = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+    w = torch.ones((T, k), dtype=torch.float32, device="cuda")
+    E, H = small["E"], small["H"]
+    q13 = torch.zeros((E, 2 * 96, H // 2), dtype=torch.uint8, device="cuda")   # I = 96: not a multiple of 128
+    s13 = torch.zeros((E, 2 * 96, H // 32), dtype=torch.uint8, device="cuda")
+    q2 = torch.zeros((E, H, 48), dtype=torch.uint8, device="cuda")
+    s2 = torch.zeros((E, H, 3), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):   # the binding finds no workspace size for I = 96
+        w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], ids, w, q13, s13, q2, s2)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(w8.W8A8Error) as e:      # and the library refuses it
+        w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], ids, w, q13, s13, q2, s2, workspace=ws)
+    assert e.value.status == 4
+    with pytest.raises(ValueError):   # scales that do not match the codes
+        w8.moe_mxfp4_grouped(dv["qx"], dv["sx"][:, :-1].contiguous(), ids, w, dv["q13"], dv["s13"], dv["q2"],
+                             dv["s2"])
+    with pytest.raises(w8.W8A8Error) as e:
+        w8.mxfp4_quantize(torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda"))   # K % 32
+    assert e.value.status == 4
