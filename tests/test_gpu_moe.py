@@ -30,6 +30,7 @@ import w8a8_fp8_linear_amd as w8  # noqa: E402
 
 SMALL = dict(T=37, H=256, I=256, E=5, k=3, n_outlier=2)
 RAGGED = dict(T=301, H=272, I=384, E=9, k=4, n_outlier=3)   # K tail, 3 gate/up tiles, odd groups
+MID = dict(T=500, H=272, I=384, E=4, k=2, n_outlier=3)       # 250 rows per group: the 128 x 128 tiles
 GATE_UP = dict(T=4096, H=2048, I=512, E=64, k=8, n_outlier=20)
 TWO_PASS = dict(T=16384, H=2048, I=512, E=64, k=8, n_outlier=20, passes=2)
 
@@ -48,6 +49,11 @@ def small():
 @pytest.fixture(scope="module")
 def ragged():
     return quantized_moe(**RAGGED, seed=11)
+
+
+@pytest.fixture(scope="module")
+def mid():
+    return quantized_moe(**MID, seed=13)
 
 
 @pytest.fixture(scope="module")
@@ -135,6 +141,11 @@ def test_gate_up_bf16_small(small):
     _check_gate_up_bf16(small)
 
 
+def test_gate_up_bf16_mid(mid):
+    """Groups of about 250 rows (the 128 x 128 tile shape)."""
+    _check_gate_up_bf16(mid)
+
+
 def test_gate_up_bf16_full_size(gate_up_cfg):
     """4096 tokens, top-8 of 64 experts, [1024 x 2048] gate+up per expert: every row."""
     _check_gate_up_bf16(gate_up_cfg)
@@ -180,6 +191,10 @@ def test_fused_requant_ragged(ragged, tile_order, row_order):
     _check_fused_requant(ragged, tile_order=tile_order, row_order=row_order)
 
 
+def test_fused_requant_mid(mid):
+    _check_fused_requant(mid)
+
+
 def test_fused_requant_gate_up_cfg(gate_up_cfg):
     _check_fused_requant(gate_up_cfg, sample=4096)
 
@@ -210,6 +225,11 @@ def test_down_combine_small(small, order):
 def test_down_combine_ragged(ragged):
     hq, hs, perm, offsets = _check_fused_requant(ragged)
     _check_down(ragged, hq, hs, perm, offsets)
+
+
+def test_down_combine_mid(mid):
+    hq, hs, perm, offsets = _check_fused_requant(mid)
+    _check_down(mid, hq, hs, perm, offsets)
 
 
 def test_down_combine_deterministic(small):
@@ -249,7 +269,7 @@ def _oracle_pass_tokens(qx, sx, ids, w, d, tokens):
     return out64
 
 
-@pytest.mark.parametrize("cfg", ["small", "ragged"])
+@pytest.mark.parametrize("cfg", ["small", "ragged", "mid"])
 def test_full_pass_small(cfg, request):
     d = request.getfixturevalue(cfg)
     dv = _dev(d)

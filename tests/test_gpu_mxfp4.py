@@ -34,6 +34,7 @@ import w8a8_fp8_linear_amd as w8  # noqa: E402
 
 SMALL = dict(T=37, H=256, I=256, E=5, k=3, n_outlier=2)
 RAGGED = dict(T=301, H=384, I=384, E=9, k=4, n_outlier=3)   # a half K stage, 3 gate/up tiles, odd groups
+MID = dict(T=500, H=384, I=384, E=4, k=2, n_outlier=3)       # 250 rows per group: the 128 x 128 tiles
 PRAXIS = dict(T=4096, H=1024, I=512, E=128, k=4, n_outlier=10, passes=2)
 
 
@@ -51,6 +52,11 @@ def small():
 @pytest.fixture(scope="module")
 def ragged():
     return quantized_mx_moe(**RAGGED, seed=11)
+
+
+@pytest.fixture(scope="module")
+def mid():
+    return quantized_mx_moe(**MID, seed=13)
 
 
 @pytest.fixture(scope="module")
@@ -145,6 +151,10 @@ def test_gate_up_bf16_ragged(ragged):
     _check_gate_up_bf16(ragged)
 
 
+def test_gate_up_bf16_mid(mid):
+    _check_gate_up_bf16(mid)
+
+
 def _check_fused(d, tile_order=0, row_order=0, sample=None):
     dv = _dev(d)
     ids, _ = d["routes"][0]
@@ -179,6 +189,10 @@ def test_fused_quant_ragged(ragged):
     _check_fused(ragged)
 
 
+def test_fused_quant_mid(mid):
+    _check_fused(mid)
+
+
 # ---- down + combine ---------------------------------------------------------------
 
 def _check_down(d, hq, hs, perm, offsets, order=0, n_tokens=None, route_idx=0):
@@ -209,6 +223,11 @@ def test_down_combine_ragged(ragged):
     _check_down(ragged, hq, hs, perm, offsets)
 
 
+def test_down_combine_mid(mid):
+    hq, hs, perm, offsets = _check_fused(mid)
+    _check_down(mid, hq, hs, perm, offsets)
+
+
 def test_down_combine_deterministic_and_order_independent(small):
     ids, tw = small["routes"][0]
     dv = _dev(small)
@@ -228,7 +247,7 @@ def _oracle_tokens(x32, ids, w, d, tokens):
     return out64
 
 
-@pytest.mark.parametrize("cfg", ["small", "ragged"])
+@pytest.mark.parametrize("cfg", ["small", "ragged", "mid"])
 def test_full_pass(cfg, request):
     d = request.getfixturevalue(cfg)
     dv = _dev(d)

@@ -598,10 +598,15 @@ int route_chunks(int64_t n) { return (int)((n + kRouteChunk - 1) / kRouteChunk);
 // for the gate/up: this shape was the fastest or within noise for both.
 constexpr int kGuBM = 256, kGuBN = 256, kGuWGM = 2, kGuWGN = 4, kGuOcc = 2;
 constexpr int kDnBM = 256, kDnBN = 256, kDnWGM = 2, kDnWGN = 4, kDnOcc = 2;
-// Groups of fewer than kSmallGroupRows rows on average (few tokens per
-// expert, e.g. 128 experts at top-4) use 128-row tiles: with 256-row tiles
-// most of each tile would be padding.
-constexpr int64_t kSmallGroupRows = 512;
+// Smaller groups (few tokens per expert, e.g. 128 or 192 experts at top-4)
+// take smaller tiles: with 256-row tiles most of each tile would be padding,
+// and a pass has too few tiles to fill the chip. Below kSmallGroupRows rows
+// on average: 128 x 128 tiles of 2 x 2 waves; below kTinyGroupRows: 64 x 128
+// tiles of 1 x 2 waves (three workgroups per CU). Timed at 4096 tokens with
+// 128 and 192 experts (128 and 85 rows per group) and at 8192 and 12288
+// tokens with 128 experts (256 and 384 rows) against 128 x 256, 64 x 256,
+// 64 x 64 and 4-wave 64 x 128 tiles.
+constexpr int64_t kSmallGroupRows = 512, kTinyGroupRows = 192;
 
 
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
@@ -618,7 +623,8 @@ hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
 // One grouped launch in the tile shape that suits the average group size.
 template <int MODE>
 hipError_t run_grouped_auto(const GroupedArgs& a, int64_t max_rows, int64_t avg_rows, hipStream_t stream) {
-  if (avg_rows < kSmallGroupRows) return run_grouped<128, 256, 2, 4, MODE, 2>(a, max_rows, stream);
+  if (avg_rows < kTinyGroupRows) return run_grouped<64, 128, 1, 2, MODE, 2>(a, max_rows, stream);
+  if (avg_rows < kSmallGroupRows) return run_grouped<128, 128, 2, 2, MODE, 2>(a, max_rows, stream);
   if (MODE == kDownY) return run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, MODE, kDnOcc>(a, max_rows, stream);
   return run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, MODE, kGuOcc>(a, max_rows, stream);
 }

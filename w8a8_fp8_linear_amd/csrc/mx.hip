@@ -450,9 +450,10 @@ __global__ __launch_bounds__(256) void combine_mx(const uint16_t* __restrict__ y
   }
 }
 
-// Tile shapes as for the FP8 experts: 256 x 256 tiles of 8 waves, and
-// 128-row tiles when groups average fewer than 512 rows.
-constexpr int64_t kMxSmallGroupRows = 512;
+// Tile shapes as for the FP8 experts: 256 x 256 tiles of 8 waves; 128 x 128
+// tiles of 2 x 2 waves when groups average fewer than 512 rows, and 64 x 128
+// tiles of 1 x 2 waves below 192 rows.
+constexpr int64_t kMxSmallGroupRows = 512, kMxTinyGroupRows = 192;
 
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 hipError_t run_mx(MxArgs a, int64_t max_rows, hipStream_t stream) {
@@ -467,7 +468,8 @@ hipError_t run_mx(MxArgs a, int64_t max_rows, hipStream_t stream) {
 
 template <int MODE>
 hipError_t run_mx_auto(const MxArgs& a, int64_t max_rows, int64_t avg_rows, hipStream_t stream) {
-  if (avg_rows < kMxSmallGroupRows) return run_mx<128, 256, 2, 4, MODE, 2>(a, max_rows, stream);
+  if (avg_rows < kMxTinyGroupRows) return run_mx<64, 128, 1, 2, MODE, 2>(a, max_rows, stream);
+  if (avg_rows < kMxSmallGroupRows) return run_mx<128, 128, 2, 2, MODE, 2>(a, max_rows, stream);
   return run_mx<256, 256, 2, 4, MODE, 2>(a, max_rows, stream);
 }
 
