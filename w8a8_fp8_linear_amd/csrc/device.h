@@ -148,6 +148,21 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
 
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// A workgroup barrier that orders LDS only: this wave's LDS accesses are
+// complete, then all waves meet. Unlike __syncthreads() it does not wait for
+// the wave's outstanding global loads and stores (on this GPU one counter
+// covers both), so stores can drain while the workgroup moves on. The empty
+// asm keeps the compiler from moving memory accesses across, the scheduling
+// barriers keep other instructions on their side.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 // Round-robin dispatch puts workgroup b on XCD b % 8. Renumber so that
 // each XCD gets a contiguous run of tile ids, then walk tile ids in groups
 // of G tile rows so that concurrently running tiles share A and W panels.
@@ -171,5 +186,13 @@ __device__ inline void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int&
 // lanes of a group read 8 consecutive rows at the same logical chunk, and
 // the XOR with (row & 7) puts them on 8 different 16-byte bank groups.
 __device__ inline int stage_off(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
+// One MFMA operand fragment from a staged K slice: chunks c and c + 4 of
+// row `row`.
+__device__ inline v8i lds_frag(const uint8_t* st, int row, int c) {
+  const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, c));
+  const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, c + 4));
+  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
 
 }  // namespace w8a8

@@ -8,12 +8,13 @@
 //
 // Two kernels:
 //  * gemm_tiled: many tokens (prompt reading). A workgroup of WGM x WGN
-//    waves owns a BM x BN output tile (256 x 192 with 2 x 4 waves: two waves
-//    per SIMD, so one wave's LDS reads overlap the other's MFMAs). Each
-//    128-deep K step of both operand tiles is copied global -> LDS by buffer
-//    loads that write LDS directly (no VGPR staging), double-buffered; each
-//    wave runs 16x16x128 E4M3 MFMAs on its (BM/WGM) x (BN/WGN) sub-tile with
-//    fp32 accumulators. The epilogue applies
+//    waves owns a BM x BN output tile (256 x 192 with 2 x 4 waves, two waves
+//    per SIMD). Each 128-deep K step of both operand tiles is copied
+//    global -> LDS by buffer loads that write LDS directly (no VGPR
+//    staging), double-buffered; each wave runs 16x16x128 E4M3 MFMAs on its
+//    (BM/WGM) x (BN/WGN) sub-tile with fp32 accumulators. The two wave
+//    groups run a ping-pong schedule: one reads its fragments from LDS while
+//    the other issues MFMAs, then they swap. The epilogue applies
 //    both scales in fp32, rounds to BF16 and goes through LDS so that every
 //    global store is a full 16-byte row segment. Workgroup ids are renumbered
 //    so that each of the 8 XCDs walks a compact block of tiles (its own L2).
@@ -51,13 +52,15 @@ struct Tiled {
   static constexpr int SM = WM / 16, SN = WN / 16;     // 16x16 MFMA tiles per wave
   static constexpr int kRows = BM + BN;                // rows of one K-slice stage
   static constexpr int kStage = kRows * 128;           // bytes per stage
-  static constexpr int kRowsPerPass = kThreads / 8;    // rows one load instruction covers
-  static constexpr int kLoadsW = BN / kRowsPerPass;    // W loads per thread per stage
-  static constexpr int kLoads = kRows / kRowsPerPass;  // all loads per thread per stage
+  static constexpr int kLoaders = kThreads / 2;        // wave group 0 issues the loads
+  static constexpr int kRowsPerPass = kLoaders / 8;    // rows one load instruction covers
+  static constexpr int kLoadsW = BN / kRowsPerPass;    // W loads per loading thread per stage
+  static constexpr int kLoads = kRows / kRowsPerPass;  // all loads per loading thread per stage
   static constexpr int kEpiStride = BN * 2 + 16;       // bytes per staged output row
   static constexpr int kEpi = BM * kEpiStride;
   static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
-  static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
+  static_assert(WGM == 2, "the ping-pong schedule needs two wave groups");
+  static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the loaders");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
 };
 
@@ -76,11 +79,23 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
   const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
   const auto rA = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
 
-  // Loader: slot s = tid + kThreads * i is a 16-byte LDS slot; rows 0..BN-1
-  // of a stage hold W, rows BN.. hold A. Lanes of a wave fill consecutive
-  // slots (8 rows of 128 bytes) and pick the global chunk that belongs in
-  // their slot. Slot s holds row (tid >> 3) + kRowsPerPass * i, and its
-  // logical chunk (tid & 7) ^ (row & 7) does not depend on i.
+  // Ping-pong schedule. Wave group 0 (waves 0..WGN-1, the tile's top BM/2
+  // rows) and group 1 (the rest) hold one wave per SIMD each and alternate:
+  // while one group reads its fragments of a K step from LDS, the other runs
+  // the MFMAs of the step it read before, so each SIMD's matrix unit is fed
+  // while its other wave reads. Group 0 also issues every global -> LDS load,
+  // one K step ahead. Step kt's stage is read by group 0 in phase 2 kt and by
+  // group 1 in phase 2 kt + 1; the loads of step kt + 1 go to the other
+  // stage at the start of phase 2 kt (both groups finished reading it by the
+  // end of phase 2 kt - 1) and are waited for at the end of phase 2 kt + 1.
+  // Every wave passes 2 nk + 2 barriers.
+  //
+  // Loader (group 0's threads, tid < kLoaders): slot s = tid + kLoaders * i
+  // is a 16-byte LDS slot; rows 0..BN-1 of a stage hold W, rows BN.. hold A.
+  // Lanes of a wave fill consecutive slots (8 rows of 128 bytes) and pick
+  // the global chunk that belongs in their slot. Slot s holds row
+  // (tid >> 3) + kRowsPerPass * i, and its logical chunk
+  // (tid & 7) ^ (row & 7) does not depend on i.
   const int lchunk = ((tid & 7) ^ ((tid >> 3) & 7)) << 4;
   const uint32_t lbase = (uint32_t)(tid >> 3) * (uint32_t)K + (uint32_t)lchunk;
   auto issue = [&](int stage, int k0) {
@@ -88,7 +103,7 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     const bool kin = k0 + lchunk < K;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-      const int s0 = wave * 64 + C::kThreads * i;  // first slot of this wave's 64
+      const int s0 = wave * 64 + C::kLoaders * i;  // first slot of this wave's 64
       const int ii = i < C::kLoadsW ? i : i - C::kLoadsW;
       const uint32_t off =
           kin ? lbase + (uint32_t)(C::kRowsPerPass * ii) * (uint32_t)K + (uint32_t)k0 : kOutOfRange;
@@ -97,7 +112,8 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     }
   };
 
-  const int wm = wave % WGM, wn = wave / WGM;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const bool loader = wm == 0;
   const int r16 = lane & 15, g = lane >> 4;
   v4f acc[C::SN][C::SM];
 #pragma unroll
@@ -106,13 +122,16 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (K + 127) >> 7;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  v8i xf[C::SM], wf[C::SN];
+  if (loader) {
+    issue(0, 0);
     wait_vmem_all();
-    __syncthreads();
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
+  }
+  lds_barrier();
+  if (!loader) lds_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (loader && kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
     const uint8_t* st = smem + (kt & 1) * C::kStage;
-    v8i xf[C::SM];
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int row = BN + wm * C::WM + j * 16 + r16;
@@ -125,16 +144,23 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
       const int row = wn * C::WN + i * 16 + r16;
       const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
       const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
-      const v8i wf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-      for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf, xf[j], acc[i][j]);
+      wf[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < C::SN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf[i], xf[j], acc[i][j]);
+    if (loader) wait_vmem_all();
+    lds_barrier();
   }
+  if (loader) lds_barrier();
 
   // Epilogue. acc[i][j][r] is Y[m][n] with m = m-tile j, lane % 16 and
   // n = n-tile i, 4 * (lane / 16) + r: four consecutive outputs of one row.
-  __syncthreads();
+  // all scale loads are issued before the barrier, and waited for together
   float sA[C::SM];
+  float4 sWv[C::SN];
 #pragma unroll
   for (int j = 0; j < C::SM; ++j) {
     const int m = m0 + wm * C::WM + j * 16 + r16;
@@ -143,8 +169,13 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
 #pragma unroll
   for (int i = 0; i < C::SN; ++i) {
     const int nl = wn * C::WN + i * 16 + 4 * g;
-    float4 sW = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (n0 + nl < N) sW = *reinterpret_cast<const float4*>(sw + n0 + nl);
+    sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(sw + n0 + nl) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C::SN; ++i) {
+    const int nl = wn * C::WN + i * 16 + 4 * g;
+    const float4 sW = sWv[i];
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
