@@ -260,10 +260,13 @@ template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
   using C = Grouped<BM, BN, WGM, WGN, MODE>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
-  __shared__ int row_tok[BM];     // token of each tile row (-1 = empty row)
-  __shared__ float row_scale[BM]; // A scale (times the router weight for DOWN)
-  __shared__ int row_dst[BM];     // GATE_UP_H: output row (-1 = none)
+  // One LDS object: the stages (or the epilogue's staging), then the row
+  // tables. With a single object the compiler does not make the LDS reads
+  // of a K step wait for the next step's direct-to-LDS loads.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds + BM * 12];
+  int* const row_tok = reinterpret_cast<int*>(smem + C::kLds);                // token of each tile row (-1 = empty)
+  float* const row_scale = reinterpret_cast<float*>(smem + C::kLds + BM * 4); // A scale (times the router weight for DOWN)
+  int* const row_dst = reinterpret_cast<int*>(smem + C::kLds + BM * 8);       // GATE_UP_H: output row (-1 = none)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N, K = p.K;
@@ -362,18 +365,10 @@ void grouped_tiled(const GroupedArgs p) {
     const uint8_t* st = smem + (kt & 1) * C::kStage;
     v8i xf[C::SM];
 #pragma unroll
-    for (int j = 0; j < C::SM; ++j) {
-      const int row = BN + wm * C::WM + j * 16 + r16;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
-      const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
-      xf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
+    for (int j = 0; j < C::SM; ++j) xf[j] = lds_frag(st, BN + wm * C::WM + j * 16 + r16, g);
 #pragma unroll
     for (int i = 0; i < C::SN; ++i) {
-      const int row = wn * C::WN + i * 16 + r16;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
-      const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
-      const v8i wf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const v8i wf = lds_frag(st, wn * C::WN + i * 16 + r16, g);
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf, xf[j], acc[i][j]);
     }
@@ -385,12 +380,18 @@ void grouped_tiled(const GroupedArgs p) {
     // Scale and round to BF16, stage in LDS, then store whole row segments:
     // measured 12% faster for this stage than 8-byte stores straight from
     // registers (each of those writes 32 bytes of 16 scattered rows).
+    float4 sWv[C::SN];  // the weight scales, loaded together before the barrier
+#pragma unroll
+    for (int i = 0; i < C::SN; ++i) {
+      const int nl = wn * C::WN + i * 16 + 4 * g;
+      sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < C::SN; ++i) {
       const int nl = wn * C::WN + i * 16 + 4 * g;
-      float4 sW = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (n0 + nl < N) sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl);
+      const float4 sW = sWv[i];
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) {
         const int ml = wm * C::WM + j * 16 + r16;
@@ -423,12 +424,18 @@ void grouped_tiled(const GroupedArgs p) {
       rs[j] = row_scale[ml];
       amax[j] = 0.f;
     }
+    float4 gsv[C::SN / 2], usv[C::SN / 2];  // gate and up scales, loaded together
+#pragma unroll
+    for (int i = 0; i < C::SN; i += 2) {
+      const int hc = (n0 >> 1) + (((wn * C::WN + i * 16) >> 5) << 4) + 4 * g;
+      gsv[i / 2] = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + hc);
+      usv[i / 2] = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + Ih + hc);
+    }
 #pragma unroll
     for (int i = 0; i < C::SN; i += 2) {  // i: gate block, i + 1: its up block
       const int sr = wn * C::WN + i * 16;
       const int hc = (n0 >> 1) + ((sr >> 5) << 4) + 4 * g;  // h column of this lane's first value
-      const float4 gs4 = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + hc);
-      const float4 us4 = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + Ih + hc);
+      const float4 gs4 = gsv[i / 2], us4 = usv[i / 2];
       const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w}, us[4] = {us4.x, us4.y, us4.z, us4.w};
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) {
@@ -456,12 +463,18 @@ void grouped_tiled(const GroupedArgs p) {
     return;
   }
   // GATE_UP: scale, round to BF16, stage in LDS, store full row segments
+  float4 sWv[C::SN];  // the weight scales, loaded together before the barrier
+#pragma unroll
+  for (int i = 0; i < C::SN; ++i) {
+    const int nl = wn * C::WN + i * 16 + 4 * g;
+    sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < C::SN; ++i) {
     const int nl = wn * C::WN + i * 16 + 4 * g;
-    float4 sW = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (n0 + nl < N) sW = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl);
+    const float4 sW = sWv[i];
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;

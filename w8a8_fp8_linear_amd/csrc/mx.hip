@@ -177,10 +177,13 @@ template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void mx_grouped(const MxArgs p) {
   using C = MxTile<BM, BN, WGM, WGN, MODE>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
-  __shared__ int row_tok[BM];     // token (gate/up) or slot (down) of each tile row, -1 = empty
-  __shared__ float row_w[BM];     // DOWN_Y: router weight of the row's slot
-  __shared__ int row_dst[BM];     // GATE_UP_Q: output row (-1 = none)
+  // One LDS object: the stages (or the epilogue's staging), then the row
+  // tables. With a single object the compiler does not make the LDS reads
+  // of a K step wait for the next step's direct-to-LDS loads.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds + BM * 12];
+  int* const row_tok = reinterpret_cast<int*>(smem + C::kLds);             // token (gate/up) or slot (down), -1 = empty
+  float* const row_w = reinterpret_cast<float*>(smem + C::kLds + BM * 4);  // DOWN_Y: router weight of the row's slot
+  int* const row_dst = reinterpret_cast<int*>(smem + C::kLds + BM * 8);    // GATE_UP_Q: output row (-1 = none)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N, Kb = p.K >> 1, Ks = p.K >> 5;
