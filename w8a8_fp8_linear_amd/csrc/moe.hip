@@ -285,25 +285,33 @@ void grouped_tiled(const GroupedArgs p) {
   const int e = grp % p.Eids;
   const int n0 = nt * BN;
 
-  for (int i = tid; i < BM; i += C::kThreads) {
-    int tok = -1, dst = -1;
-    float sc = 0.f;
-    if (i < rows) {
-      const int slot = p.perm[row0 + i];
-      if (slot >= 0 && slot < cap) {
-        tok = MODE == kDownY ? slot : slot / p.topk;  // DOWN_Y keeps the slot: its output row
-        sc = kIsDown ? p.sA[row0 + i] * p.tw[slot] : p.sA[tok];
-        if (MODE == kGateUpH) {
-          dst = p.dst_row ? p.dst_row[slot] : row0 + i;
-          if (dst >= cap) dst = -1;
+  // The row tables. A down-projection tile reads contiguous rows, so its
+  // first stage of loads is issued before these (their loads overlap); the
+  // first barrier of the K loop orders the tables before their use.
+  auto setup_rows = [&]() {
+    for (int i = tid; i < BM; i += C::kThreads) {
+      int tok = -1, dst = -1;
+      float sc = 0.f;
+      if (i < rows) {
+        const int slot = p.perm[row0 + i];
+        if (slot >= 0 && slot < cap) {
+          tok = MODE == kDownY ? slot : slot / p.topk;  // DOWN_Y keeps the slot: its output row
+          sc = kIsDown ? p.sA[row0 + i] * p.tw[slot] : p.sA[tok];
+          if (MODE == kGateUpH) {
+            dst = p.dst_row ? p.dst_row[slot] : row0 + i;
+            if (dst >= cap) dst = -1;
+          }
         }
       }
+      row_tok[i] = tok;
+      row_scale[i] = sc;
+      row_dst[i] = dst;
     }
-    row_tok[i] = tok;
-    row_scale[i] = sc;
-    row_dst[i] = dst;
+  };
+  if (!kIsDown) {
+    setup_rows();
+    __syncthreads();
   }
-  __syncthreads();
 
   const auto rB = MODE == kGateUpH ? make_rsrc(p.B + (int64_t)e * N * K, (int64_t)N * K)
                                     : make_rsrc(p.B + ((int64_t)e * N + n0) * K, (int64_t)(N - n0) * K);
@@ -358,6 +366,7 @@ void grouped_tiled(const GroupedArgs p) {
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (K + 127) >> 7;
   issue(0, 0);
+  if (kIsDown) setup_rows();
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmem_all();
     __syncthreads();

@@ -199,25 +199,33 @@ void mx_grouped(const MxArgs p) {
   const int e = grp % p.Eids;
   const int n0 = nt * BN;
 
-  for (int i = tid; i < BM; i += C::kThreads) {
-    int tok = -1, dst = -1;
-    float w = 0.f;
-    if (i < rows) {
-      const int slot = p.perm[row0 + i];
-      if (slot >= 0 && slot < cap) {
-        tok = kIsDown ? slot : slot / p.topk;
-        if (kIsDown) w = p.tw[slot];
-        if (MODE == kMxGateUpQ) {
-          dst = p.dst_row ? p.dst_row[slot] : row0 + i;
-          if (dst >= cap) dst = -1;
+  // The row tables. A down-projection tile reads contiguous rows, so its
+  // first stage of loads is issued before these (their loads overlap); the
+  // first barrier of the K loop orders the tables before their use.
+  auto setup_rows = [&]() {
+    for (int i = tid; i < BM; i += C::kThreads) {
+      int tok = -1, dst = -1;
+      float w = 0.f;
+      if (i < rows) {
+        const int slot = p.perm[row0 + i];
+        if (slot >= 0 && slot < cap) {
+          tok = kIsDown ? slot : slot / p.topk;
+          if (kIsDown) w = p.tw[slot];
+          if (MODE == kMxGateUpQ) {
+            dst = p.dst_row ? p.dst_row[slot] : row0 + i;
+            if (dst >= cap) dst = -1;
+          }
         }
       }
+      row_tok[i] = tok;
+      row_w[i] = w;
+      row_dst[i] = dst;
     }
-    row_tok[i] = tok;
-    row_w[i] = w;
-    row_dst[i] = dst;
+  };
+  if (!kIsDown) {
+    setup_rows();
+    __syncthreads();
   }
-  __syncthreads();
 
   const int64_t eN = (int64_t)e * N;
   const bool whole_b = MODE == kMxGateUpQ;  // interleaved gate/up rows address the expert's whole W13
@@ -300,6 +308,7 @@ void mx_grouped(const MxArgs p) {
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (Kb + 127) >> 7;
   issue(0, 0);
+  if (kIsDown) setup_rows();
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmem_all();
     __syncthreads();
