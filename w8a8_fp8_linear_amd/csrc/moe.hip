@@ -615,9 +615,9 @@ int route_chunks(int64_t n) { return (int)((n + kRouteChunk - 1) / kRouteChunk);
 
 // Tile shapes (both on expert-major groups of about T*k/E rows): 256 x 256
 // tiles, 8 waves of 128 x 64, two waves per SIMD. Measured on the 16384-token
-// two-pass workload against 128 x 256 (8 waves) and 128 x 128 (4 waves, two
-// workgroups per CU) for the down projection, and 128 x 256 and 4 x 2 waves
-// for the gate/up: this shape was the fastest or within noise for both.
+// two-pass workload against 128 x 256, 256 x 128 and 128 x 128 tiles for the
+// gate/up, and 128 x 256, 128 x 128 and a persistent variant with split
+// load / store roles for the down projection: this shape was the fastest.
 constexpr int kGuBM = 256, kGuBN = 256, kGuWGM = 2, kGuWGN = 4, kGuOcc = 2;
 constexpr int kDnBM = 256, kDnBN = 256, kDnWGM = 2, kDnWGN = 4, kDnOcc = 2;
 // Smaller groups (few tokens per expert, e.g. 128 or 192 experts at top-4)
