@@ -146,6 +146,17 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// 16-byte stores of large write-once outputs (the GEMM's Y, the routed
+// copies' y rows, the float32 h rows) with the non-temporal hint: they are
+// streamed out rather than kept in the L2 of the writing XCD. Measured 6-11%
+// faster for the down projection, about 1% for the prefill GEMM.
+__device__ inline void store16_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<v4i*>(p));
+}
+__device__ inline void store16_nt(void* p, float4 v) {
+  __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
+}
+
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // A workgroup barrier that orders LDS only: this wave's LDS accesses are

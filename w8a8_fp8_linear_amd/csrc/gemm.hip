@@ -191,8 +191,7 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     const int m = m0 + row, n = n0 + col;
     if (m < M && n < N)
-      *reinterpret_cast<uint4*>(Y + (int64_t)m * N + n) =
-          *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
+      store16_nt(Y + (int64_t)m * N + n, *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
   }
 }
 

@@ -417,8 +417,8 @@ void grouped_tiled(const GroupedArgs p) {
       const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
       const int slot = row_tok[row];
       if (slot >= 0 && n0 + col < N)
-        *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)slot * N + n0 + col) =
-            *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
+        store16_nt(p.out_bf16 + (int64_t)slot * N + n0 + col,
+                   *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
     }
     return;
   }
@@ -458,7 +458,7 @@ void grouped_tiled(const GroupedArgs p) {
           amax[j] = fmaxf(amax[j], fabsf(h[r]));
         }
         if (dsts[j] >= 0)
-          *reinterpret_cast<float4*>(p.out_f32 + (int64_t)dsts[j] * Ih + hc) = make_float4(h[0], h[1], h[2], h[3]);
+          store16_nt(p.out_f32 + (int64_t)dsts[j] * Ih + hc, make_float4(h[0], h[1], h[2], h[3]));
       }
     }
     // lane groups g = 0..3 hold the same rows: reduce over them, one atomic per row
@@ -499,8 +499,8 @@ void grouped_tiled(const GroupedArgs p) {
   for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     if (row < rows && n0 + col < N)
-      *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)(row0 + row) * N + n0 + col) =
-          *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
+      store16_nt(p.out_bf16 + (int64_t)(row0 + row) * N + n0 + col,
+                 *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
   }
 }
 

@@ -366,8 +366,8 @@ void mx_grouped(const MxArgs p) {
       const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
       const int slot = row_tok[row];
       if (slot >= 0 && n0 + col < N)
-        *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)slot * N + n0 + col) =
-            *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
+        store16_nt(p.out_bf16 + (int64_t)slot * N + n0 + col,
+                   *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
     }
     return;
   }
@@ -433,8 +433,8 @@ void mx_grouped(const MxArgs p) {
   for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     if (row < rows && n0 + col < N)
-      *reinterpret_cast<uint4*>(p.out_bf16 + (int64_t)(row0 + row) * N + n0 + col) =
-          *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2);
+      store16_nt(p.out_bf16 + (int64_t)(row0 + row) * N + n0 + col,
+                 *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
   }
 }
 
