@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
     v4i t = v4i{0, 0, 0, 0};
-    if (c < nch) t = __builtin_nontemporal_load(xr + c);
+    if (c < nch) t = xr[c];
     v[i] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
   }
 #pragma unroll
