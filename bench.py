@@ -361,6 +361,30 @@ def _avg_ms(evs):
     return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
 
+def _graph_us(fn, reps=10, warmup=3):
+    """fn captured once into a HIP graph, then `reps` replays between HIP
+    events: the time per call without the host's launch overhead (every
+    kernel of fn still runs each replay)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = _events(reps)
+    for a, b in evs:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * _avg_ms(evs)
+    del g
+    return us
+
+
 def _moe_inputs(cfg):
     import torch
 
@@ -432,6 +456,7 @@ def bench_moe_two_pass(reps=5, warmup=2):
         b.record(stream)
     torch.cuda.synchronize()
     ms = _avg_ms(evs)
+    us_graph = _graph_us(lambda: w8.moe_ffn(x, routes, q13, s13, q2, s2, workspace=ws), reps=reps)
     flops_pass = 2.0 * T * k * 2 * I * H + 2.0 * T * k * H * I
     flops = 2 * flops_pass
     # per-stage split of one pass, each stage timed on its own
@@ -472,7 +497,7 @@ def bench_moe_two_pass(reps=5, warmup=2):
             "us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "frac_fp8_peak": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, "flops": flops,
             "roofline_us": flops / (FP8_PEAK_TFLOPS * 1e12) * 1e6,
-            "tokens_per_s": T / (ms * 1e-3), "stage_us_one_pass": stages}
+            "tokens_per_s": T / (ms * 1e-3), "us_graph_replay": us_graph, "stage_us_one_pass": stages}
 
 
 def bench_moe_pages_shapes(reps=10, warmup=3):
@@ -498,10 +523,12 @@ def bench_moe_pages_shapes(reps=10, warmup=3):
             b.record(stream)
         torch.cuda.synchronize()
         ms = _avg_ms(evs)
+        us_graph = _graph_us(lambda: w8.moe_ffn(x, routes, q13, s13, q2, s2, workspace=ws), reps=reps)
         flops = 2 * (2.0 * T * k * 2 * I * H + 2.0 * T * k * H * I)
         out[cfg["name"]] = {"us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
                             "frac_fp8_peak": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-                            "tokens_per_s": T / (ms * 1e-3)}
+                            "tokens_per_s": T / (ms * 1e-3), "us_graph_replay": us_graph,
+                            "tflops_graph_replay": flops / (us_graph * 1e-6) / 1e12}
     return out
 
 
@@ -546,9 +573,11 @@ def bench_moe_mxfp4(reps=10, warmup=3):
             b.record(stream)
         torch.cuda.synchronize()
         ms = _avg_ms(evs)
+        us_graph = _graph_us(lambda: w8.moe_mxfp4_ffn(x, routes, q13, s13, q2, s2, workspace=ws), reps=reps)
         flops = 2 * (2.0 * T * k * 2 * I * H + 2.0 * T * k * H * I)
         rec = {"us_avg": 1e3 * ms, "tflops": flops / (ms * 1e-3) / 1e12,
-               "frac_fp4_peak": flops / (ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, "tokens_per_s": T / (ms * 1e-3)}
+               "frac_fp4_peak": flops / (ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, "tokens_per_s": T / (ms * 1e-3),
+               "us_graph_replay": us_graph, "tflops_graph_replay": flops / (us_graph * 1e-6) / 1e12}
         if cfg is synth.MOE_TWO_PASS:
             xq, xs = w8.mxfp4_quantize(x)
             ids, tw = routes[0]
