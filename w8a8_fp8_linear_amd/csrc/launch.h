@@ -40,8 +40,10 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t t
 size_t gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk);
 
 // slot_row (may be NULL): slot -> its sorted row, -1 for a dropped id.
+// zero (may be NULL): zero_n words the same launch clears.
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int order, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* slot_row, void* scratch, hipStream_t stream);
+                        int32_t* offsets, int32_t* perm, int32_t* slot_row, void* scratch, hipStream_t stream,
+                        uint32_t* zero = nullptr, int64_t zero_n = 0);
 
 hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const uint8_t* w13, const float* s13,
@@ -49,12 +51,14 @@ hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const
                                        int64_t topk, int order, hipStream_t stream);
 
 // dst_row (may be NULL): slot -> output row of h_q / h_scale; NULL keeps
-// the sorted order of perm. ws: gate_up_swiglu_quant_workspace_bytes bytes.
+// the sorted order of perm. ws: gate_up_swiglu_quant_workspace_bytes bytes,
+// whose first T * topk words (the row maxima) it clears first unless
+// amax_zeroed says an earlier launch on the stream already did.
 hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
                                        const float* s13, uint8_t* qh, float* sh, int64_t T, int64_t H,
                                        int64_t I, int64_t E, int64_t topk, int order, void* ws,
-                                       hipStream_t stream);
+                                       hipStream_t stream, bool amax_zeroed = false);
 
 // y: [T*topk, H] BF16 scratch (down_combine_scratch_bytes).
 size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk);

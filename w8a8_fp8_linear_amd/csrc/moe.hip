@@ -104,13 +104,30 @@ __global__ __launch_bounds__(256) void route_count(const int32_t* __restrict__ i
 __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__ ids, int64_t n, int Eids, int kdiv,
                                                      int E, int nchunks, const int32_t* __restrict__ chunk_counts,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm, int32_t* __restrict__ slot_row) {
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ slot_row,
+                                                     uint32_t* __restrict__ zero, int64_t zero_n) {
   extern __shared__ int sm[];
+  // side job for the full pass: clear the gate/up stage's row maxima
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < zero_n; i += (int64_t)gridDim.x * 256) zero[i] = 0;
   int* before = sm;              // slots of expert e in earlier chunks, plus the expert's offset
   int* base = sm + E;            // per wave running position
   int* whist = sm + 5 * E;       // per wave histogram of its sub-chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
+  // this wave's keys, loaded once up front so that their latency overlaps
+  // the chunk-count reads (E + 1: dropped id, E + 2: past the end)
+  const int64_t sub0 = (int64_t)c * kRouteChunk + (int64_t)wave * kRouteSub;
+  int keys[kRouteSub / 64];
+#pragma unroll
+  for (int i = 0; i < kRouteSub / 64; ++i) {
+    const int64_t s = sub0 + 64 * i + lane;
+    int key = E + 1;
+    if (s < n) {
+      const int k2 = group_key(s, ids[s], Eids, kdiv);
+      key = k2 >= 0 ? k2 : E;
+    }
+    keys[i] = key;
+  }
   for (int e = tid; e < 4 * E; e += 256) whist[e] = 0;
   // group totals and the counts of earlier chunks: every thread takes groups
   // tid, tid + 256, ...; the exclusive scan over groups is then done by wave 0
@@ -154,15 +171,10 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
   }
   __syncthreads();
   const int nbits = bits_for(E + 1);
-  const int64_t sub0 = (int64_t)c * kRouteChunk + (int64_t)wave * kRouteSub;
   // pass 1: histogram of this wave's sub-chunk
-  for (int i = 0; i < kRouteSub; i += 64) {
-    const int64_t s = sub0 + i + lane;
-    int key = E + 1;
-    if (s < n) {
-      const int k2 = group_key(s, ids[s], Eids, kdiv);
-      key = k2 >= 0 ? k2 : E;
-    }
+#pragma unroll
+  for (int i = 0; i < kRouteSub / 64; ++i) {
+    const int key = keys[i];
     const uint64_t peers = match_peers(key, nbits);
     const bool leader = lane == 63 - __clzll(peers);
     if (leader && key < E) whist[wave * E + key] += __popcll(peers);
@@ -178,13 +190,10 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
   __syncthreads();
   // pass 2: stable scatter
   const uint64_t lt = (1ull << lane) - 1;
-  for (int i = 0; i < kRouteSub; i += 64) {
-    const int64_t s = sub0 + i + lane;
-    int key = E + 1;
-    if (s < n) {
-      const int k2 = group_key(s, ids[s], Eids, kdiv);
-      key = k2 >= 0 ? k2 : E;
-    }
+#pragma unroll
+  for (int i = 0; i < kRouteSub / 64; ++i) {
+    const int64_t s = sub0 + 64 * i + lane;
+    const int key = keys[i];
     const uint64_t peers = match_peers(key, nbits);
     if (key < E) {
       const int pos = base[wave * E + key] + __popcll(peers & lt);
@@ -679,7 +688,8 @@ size_t route_workspace_bytes(int64_t T, int64_t topk, int64_t G) {
 int64_t route_groups(int64_t topk, int64_t E, int order) { return order ? topk * E : E; }
 
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, int order, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* slot_row, void* scratch, hipStream_t stream) {
+                        int32_t* offsets, int32_t* perm, int32_t* slot_row, void* scratch, hipStream_t stream,
+                        uint32_t* zero, int64_t zero_n) {
   const int64_t n = T * topk;
   const int nch = route_chunks(n);
   if (nch == 0) return hipSuccess;
@@ -689,7 +699,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t topk, int64_t E, 
   hipLaunchKernelGGL(route_count, dim3(nch), dim3(256), (size_t)G * 4, stream, ids, n, (int)E, kdiv, G,
                      chunk_counts);
   hipLaunchKernelGGL(route_scatter, dim3(nch), dim3(256), (size_t)G * 9 * 4, stream, ids, n, (int)E, kdiv, G, nch,
-                     chunk_counts, counts, offsets, perm, slot_row);
+                     chunk_counts, counts, offsets, perm, slot_row, zero, zero_n);
   return hipGetLastError();
 }
 
@@ -711,13 +721,14 @@ size_t gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk) 
 hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
                                        const float* s13, uint8_t* qh, float* sh, int64_t T, int64_t H, int64_t I,
-                                       int64_t E, int64_t topk, int order, void* ws, hipStream_t stream) {
+                                       int64_t E, int64_t topk, int order, void* ws, hipStream_t stream,
+                                       bool amax_zeroed) {
   const int64_t n = T * topk;
   if (n == 0) return hipSuccess;
   const int G = (int)route_groups(topk, E, order);
   uint32_t* amax = static_cast<uint32_t*>(ws);
   float* h = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * 4));
-  hipLaunchKernelGGL(fill_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, amax, n);
+  if (!amax_zeroed) hipLaunchKernelGGL(fill_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, amax, n);
   GroupedArgs a = gate_up_args(xq, xs, perm, offsets, G, w13, s13, T, H, I, E, topk);
   a.out_f32 = h;
   a.row_amax = amax;
@@ -815,10 +826,12 @@ hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, co
   int32_t* perm = reinterpret_cast<int32_t*>(b + L.perm);
   uint8_t* qh = b + L.qh;
   float* sh = reinterpret_cast<float*>(b + L.sh);
-  hipError_t err = launch_route(ids, T, topk, E, 0, counts, offsets, perm, nullptr, b + L.route, stream);
+  // the routing launch also clears the gate/up stage's row maxima
+  hipError_t err = launch_route(ids, T, topk, E, 0, counts, offsets, perm, nullptr, b + L.route, stream,
+                                reinterpret_cast<uint32_t*>(b + L.amax), T * topk);
   if (err != hipSuccess) return err;
   err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, T, H, I, E, topk, 0,
-                                    b + L.amax, stream);
+                                    b + L.amax, stream, true);
   if (err != hipSuccess) return err;
   return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<uint16_t*>(b + L.big), out_q,
                              out_s, T, H, I, E, topk, 0, stream);
