@@ -232,6 +232,26 @@ def test_down_combine_mid(mid):
     _check_down(mid, hq, hs, perm, offsets)
 
 
+# Groups of 512 rows or more (the 256 x 256 tiles) on shapes the workloads
+# above do not reach: a ragged N tail, 6 and 8 K steps in the down
+# projection, one n-tile, more tiles than CUs.
+LARGE_GROUPS = [
+    dict(T=1100, H=2064, I=512, E=2, k=1, n_outlier=3),   # an N tail: 2064 = 8 x 256 + 16
+    dict(T=700, H=512, I=1024, E=1, k=1, n_outlier=2),    # 8 K steps
+    dict(T=600, H=256, I=768, E=1, k=1, n_outlier=2),     # 6 K steps, one n-tile
+    dict(T=4096, H=2048, I=512, E=2, k=2, n_outlier=4),   # 272 tiles: more than one per workgroup
+]
+
+
+@pytest.mark.parametrize("cfg", LARGE_GROUPS)
+@pytest.mark.parametrize("order", [0, 1])
+def test_down_combine_large_groups(cfg, order):
+    print(f"[large groups] {cfg} order={order}", flush=True)
+    d = quantized_moe(**cfg, seed=17)
+    hq, hs, perm, offsets = _check_fused_requant(d, tile_order=order, row_order=order, sample=2048)
+    _check_down(d, hq, hs, perm, offsets, n_tokens=min(512, d["T"]), order=order)
+
+
 def test_down_combine_deterministic(small):
     dv = _dev(small)
     ids, tw = small["routes"][0]
