@@ -133,19 +133,9 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     if (loader && kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
     const uint8_t* st = smem + (kt & 1) * C::kStage;
 #pragma unroll
-    for (int j = 0; j < C::SM; ++j) {
-      const int row = BN + wm * C::WM + j * 16 + r16;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
-      const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
-      xf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
+    for (int j = 0; j < C::SM; ++j) xf[j] = lds_frag(st, BN + wm * C::WM + j * 16 + r16, g);
 #pragma unroll
-    for (int i = 0; i < C::SN; ++i) {
-      const int row = wn * C::WN + i * 16 + r16;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + stage_off(row, g));
-      const v4i hi = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4));
-      wf[i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
+    for (int i = 0; i < C::SN; ++i) wf[i] = lds_frag(st, wn * C::WN + i * 16 + r16, g);
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < C::SN; ++i)
