@@ -164,7 +164,10 @@ def bench_prefill(steps, warmup):
 
     gemm_ms = launches_ms(lambda: w8.w8a8_gemm(xq, xs, wq, ws, out=y))
     gemm_avg = sum(gemm_ms) / len(gemm_ms)
-    q_ms = launches_ms(lambda: w8.quantize_per_token(x, xq, xs))
+    # The quantiser's ~5 us launches are shorter than one Python call, so
+    # eager back-to-back launches would time the host: replay 40 of them
+    # from a HIP graph instead.
+    q_ms, _ = _per_launch_ms([lambda: w8.quantize_per_token(x, xq, xs)] * 40, 5, stream)
     q_avg = sum(q_ms) / len(q_ms)
 
     flops = 2.0 * M * N * K

@@ -64,9 +64,11 @@ def _structured_rows(exp0=127, span=21):
     return out
 
 
-@pytest.mark.parametrize("exp0", [127, 60, 200, 21])
+@pytest.mark.parametrize("exp0", [127, 60, 200, 21, 37, 36])
 def test_quantize_every_mantissa_pair(exp0):
-    # every amax mantissa against every smaller BF16 value within 2**-20 of it
+    # every amax mantissa against every smaller BF16 value within 2**-20 of it; amax near 2**-90
+    # (exp0 37 and 36) puts the row scale just above and below 2**-99, where the kernel switches
+    # from the corrected product to the division
     _quant_check(_structured_rows(exp0=exp0), f"structured exp0={exp0}")
 
 

@@ -106,24 +106,37 @@ __device__ inline uint32_t absmax8(uint4 v) {
   return m;
 }
 
+// Smallest row scale for which quant8 takes the quotient without dividing.
+constexpr float kQuotientMinScale = 0x1p-99f;
+
 // 8 BF16 values -> 8 E4M3 codes of fl32(x / s) (little-endian, element 0 in
-// byte 0); r = fl32(1 / s), or a non-finite r (a subnormal scale) to divide
-// every value.
+// byte 0), for a row scale s = fl32(amax / 448) of a BF16 row maximum (or 1)
+// and r = fl32(1 / s), both correctly rounded divisions.
+//
+// The quotient comes from one residual correction of x * r (Markstein's
+// method, with fused multiply-adds): q0 = fl32(x * r), q = fl32(q0 +
+// fl32(x - q0 * s) * r), with the sign of x put back on a zero result. For
+// s >= 2^-99, every BF16 x with |x| <= amax and both signs, this q equals
+// fl32(x / s) bit for bit wherever |x / s| >= 2^-12, and elsewhere has
+// magnitude below 2^-11 and the sign of x, so the E4M3 code is the same
+// (an exhaustive check over all 1.07e9 (amax, x) pairs runs with the CPU
+// tests). Below 2^-99 the residual can underflow and the row divides; s is
+// one value per row, so the branch does not split a wave working on one row.
 __device__ inline uint2 quant8(uint4 v, float s, float r) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float x[8], q[8];
-  bool near = !(r < 3.0e38f);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = bf16_lo(w[i]);
     x[2 * i + 1] = bf16_hi(w[i]);
   }
+  if (__builtin_expect(s >= kQuotientMinScale, 1)) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    q[k] = x[k] * r;
-    near |= e4m3_boundary_near(q[k]);
-  }
-  if (__builtin_expect(near, 0)) {
+    for (int k = 0; k < 8; ++k) {
+      const float q0 = x[k] * r;
+      q[k] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x[k]), r, q0), x[k]);
+    }
+  } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) q[k] = x[k] / s;
   }

@@ -11,13 +11,14 @@
 // One wave per row: BF16 is read with 16-byte loads (8 values per lane per
 // load) and kept in registers, amax is a wave-wide max, then every element
 // is scaled and encoded. fl32(x / s) is obtained without a division per
-// element: v = x * r with r = fl32(1 / s) is within 2 ulp of fl32(x / s)
-// (two roundings of relative size 2^-24 each), so v and fl32(x / s) have the
-// same E4M3 code unless v is within a few ulp of a rounding boundary or in
-// the subnormal range; a lane holding such a value redoes its 8 values with
-// the correctly rounded division (so does every lane of a row whose scale is
-// so small that 1 / s overflows). The encoding itself is the hardware
-// conversion (round to nearest even) after clamping to +-448.
+// element: x * r with r = fl32(1 / s), corrected once with its fused
+// residual, is the correctly rounded quotient wherever the code depends on
+// it (quant8 states the range; rows with a scale below 2^-99 divide). The
+// encoding itself is the hardware conversion (round to nearest even) after
+// clamping to +-448. An earlier form redid a lane's values with the
+// division whenever x * r fell near a rounding boundary or below 2^-6; with
+// about 0.2% of N(0, 1) values in that range most waves took it, and the
+// 4096 x 2048 quantisation ran at 7.9 us against 4.2 us without it.
 // Rows longer than 64 * 8 * 16 values stream through twice instead.
 #include "device.h"
 #include "launch.h"
