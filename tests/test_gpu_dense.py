@@ -135,6 +135,10 @@ GEMM_SHAPES = [
     ("ragged_300x6144x128", 300, 6144, 128),
     ("tall_4096x16x2048", 4096, 16, 2048),
     ("ragged_513x1040x272", 513, 1040, 272),
+    # 17..32 rows: two 16-row weight tiles per workgroup, so an odd number of them leaves the
+    # last workgroup's second tile past N; K = 272 / 2064 end inside a 128-deep step
+    ("ragged_24x1040x272", 24, 1040, 272),
+    ("ragged_32x48x2064", 32, 48, 2064),
 ]
 
 

@@ -185,26 +185,30 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
   }
 }
 
-// Small-M kernel: 16 weight rows per workgroup, K split over the 4 waves,
-// U K-steps of loads in flight per wave. MT = number of 16-token tiles.
-template <int MT, int U>
+// Small-M kernel: NT tiles of 16 weight rows per workgroup, K split over
+// the 4 waves, U K-steps of loads in flight per wave. MT = number of 16-token
+// tiles. Every workgroup reads all M input rows (from L2), so for M > 16 two
+// weight tiles per workgroup halve that traffic; a wave's input fragments
+// serve both tiles. Each output's sum runs in the same order for any NT.
+template <int MT, int U, int NT = 1>
 __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                    const uint8_t* __restrict__ W, const float* __restrict__ sw,
                                                    uint16_t* __restrict__ Y, int M, int N, int K) {
-  __shared__ v4f red[3][MT][64];
+  __shared__ v4f red[3][NT][MT][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NT;
   const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
   const auto rA = make_rsrc(A, (int64_t)M * K);
   const int r16 = lane & 15, g = lane >> 4;
-  const uint32_t wrow = (uint32_t)r16 * (uint32_t)K;
-  v4f acc[MT];
+  v4f acc[NT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (K + 127) >> 7;
   for (int kt = wave; kt < nk; kt += 4 * U) {
-    v8i wf[U], xf[U][MT];
+    v8i wf[U][NT], xf[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k0 = (kt + 4 * u) << 7;
@@ -212,9 +216,13 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
       const bool live = kt + 4 * u < nk;
       const uint32_t o0 = (live && c0 < K) ? (uint32_t)c0 : kOutOfRange;
       const uint32_t o1 = (live && c1 < K) ? (uint32_t)c1 : kOutOfRange;
-      const v4i lo = buffer_load16(rW, o0 == kOutOfRange ? o0 : wrow + o0);
-      const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
-      wf[u] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const uint32_t wrow = (uint32_t)(i * 16 + r16) * (uint32_t)K;
+        const v4i lo = buffer_load16(rW, o0 == kOutOfRange ? o0 : wrow + o0);
+        const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
+        wf[u][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const uint32_t xrow = (uint32_t)(t * 16 + r16) * (uint32_t)K;
@@ -229,26 +237,33 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma_16x16x128_e4m3(wf[u], xf[u][t], acc[t]);
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[i][t] = mfma_16x16x128_e4m3(wf[u][i], xf[u][t], acc[i][t]);
   }
   if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[wave - 1][t][lane] = acc[t];
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) red[wave - 1][i][t][lane] = acc[i][t];
   }
   __syncthreads();
   if (wave != 0) return;
-  const int n = n0 + 4 * g;
-  if (n >= N) return;
-  const float4 sW = *reinterpret_cast<const float4*>(sw + n);
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
-    const int m = t * 16 + r16;
-    if (m < M) {
-      const float s = sa[m];
-      const uint32_t p0 = bf16x2_rne(a[0] * s * sW.x, a[1] * s * sW.y);
-      const uint32_t p1 = bf16x2_rne(a[2] * s * sW.z, a[3] * s * sW.w);
-      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
+  for (int i = 0; i < NT; ++i) {
+    const int n = n0 + i * 16 + 4 * g;
+    if (n >= N) continue;
+    const float4 sW = *reinterpret_cast<const float4*>(sw + n);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const v4f a = acc[i][t] + red[0][i][t][lane] + red[1][i][t][lane] + red[2][i][t][lane];
+      const int m = t * 16 + r16;
+      if (m < M) {
+        const float s = sa[m];
+        const uint32_t p0 = bf16x2_rne(a[0] * s * sW.x, a[1] * s * sW.y);
+        const uint32_t p1 = bf16x2_rne(a[2] * s * sW.z, a[3] * s * sW.w);
+        *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
+      }
     }
   }
 }
@@ -371,7 +386,7 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
     return hipGetLastError();
   }
   if (M <= 32) {
-    hipLaunchKernelGGL((gemm_skinny<2, 4>), dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, a, sa, w, sw,
+    hipLaunchKernelGGL((gemm_skinny<2, 4, 2>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, stream, a, sa, w, sw,
                        y, (int)M, (int)N, (int)K);
     return hipGetLastError();
   }
