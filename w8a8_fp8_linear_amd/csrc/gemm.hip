@@ -141,6 +141,10 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
     for (int i = 0; i < C::SN; ++i)
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf[i], xf[j], acc[i][j]);
+    // The wait must stay behind the MFMAs: an s_waitcnt is no scheduling
+    // barrier, and hoisted above them it would make every step wait for the
+    // loads it has just issued.
+    __builtin_amdgcn_sched_barrier(0);
     if (loader) wait_vmem_all();
     lds_barrier();
   }
