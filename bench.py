@@ -621,9 +621,11 @@ def bench_moe_mxfp4(reps=10, warmup=3):
     return out
 
 
-def cpu_baseline():
+def cpu_baseline(min_seconds=10.0):
     """The CPU oracle on the full prefill workload (activation quantisation,
-    exact float64 GEMM, BF16 rounding), timed once on this host."""
+    exact float64 GEMM, BF16 rounding), run back to back on this host until
+    at least ``min_seconds`` have passed (at least once); the figure is the
+    mean per run."""
     import numpy as np
 
     import oracle
@@ -639,13 +641,19 @@ def cpu_baseline():
     d = synth.dense_workload(**cfg, seed=0)
     qw, sw, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["w"]))
     x = synth.bf16_bits_to_f32(d["x"])
+    runs = 0
     t0 = time.perf_counter()
-    qx, sx, _ = oracle.quantize_rows(x)
-    oracle.w8a8_linear(qx, sx, qw, sw)
-    dt = time.perf_counter() - t0
+    while True:
+        qx, sx, _ = oracle.quantize_rows(x)
+        oracle.w8a8_linear(qx, sx, qw, sw)
+        runs += 1
+        total = time.perf_counter() - t0
+        if total >= min_seconds:
+            break
+    dt = total / runs
     return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full prefill workload {M}x{K} -> {N}: quantise + float64 GEMM + BF16 rounding, one run "
-                      f"({dt:.2f} s)", "seconds": dt}
+            "sample": f"full prefill workload {M}x{K} -> {N}: quantise + float64 GEMM + BF16 rounding, {runs} run{'s' if runs != 1 else ''} "
+                      f"back to back in {total:.1f} s ({dt:.2f} s per run)", "seconds": dt, "runs": runs}
 
 
 def main():
