@@ -10,7 +10,8 @@
 //
 // One wave per row: BF16 is read with 16-byte loads (8 values per lane per
 // load) and kept in registers, amax is a wave-wide max, then every element
-// is scaled and encoded. fl32(x / s) is obtained without a division per
+// is scaled and encoded (rows longer than 64 * 8 * 16 values stream through
+// twice instead). fl32(x / s) is obtained without a division per
 // element: x * r with r = fl32(1 / s), corrected once with its fused
 // residual, is the correctly rounded quotient wherever the code depends on
 // it (quant8 states the range; rows with a scale below 2^-99 divide). The
@@ -20,7 +21,6 @@
 // of the prefill activations land there after scaling, enough to send 9
 // waves in 10 into it, and the 4096 x 2048 quantisation ran at 7.8 us
 // against 4.9 us with the correction.
-// Rows longer than 64 * 8 * 16 values stream through twice instead.
 #include "device.h"
 #include "launch.h"
 
