@@ -38,10 +38,13 @@ static uint32_t bits(float f) {
 int main(int argc, char** argv) {
   const int mode = argc > 1 ? atoi(argv[1]) : 0;
   long long pairs = 0, failures = 0;
-  volatile int stop = 0;
+  int stop = 0; /* set once a planted mistake is caught; OpenMP atomics */
 #pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, failures)
   for (int a = 0; a <= 0x7F7F; ++a) {
-    if (stop) continue;
+    int stopped;
+#pragma omp atomic read
+    stopped = stop;
+    if (stopped) continue;
     const float s = a == 0 ? 1.0f : bf16((uint32_t)a) / 448.0f;
     const float r = 1.0f / s;
     const int corrected = mode == 2 || s >= 0x1p-99f;
@@ -64,7 +67,10 @@ int main(int argc, char** argv) {
         ++pairs;
         if (!ok) {
           ++failures;
-          if (mode != 0) stop = 1;
+          if (mode != 0) {
+#pragma omp atomic write
+            stop = 1;
+          }
         }
       }
     }
