@@ -230,10 +230,11 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
 
 
 def bench_decode_layer(Ms=(9, 16, 32), n_buffers=40, reps=5):
-    """The fast-math decode layer from BF16 input: fp8_linear (per-token
-    quantisation launch + GEMM launch) against fp8_linear_single_launch (the
-    quantisation fused into the GEMM), HIP-graph replayed over 40 rotated
-    weight copies."""
+    """The fast-math decode layer from BF16 input, HIP-graph replayed over 40
+    rotated weight copies: the two-launch chain (quantize_per_token into a
+    buffer + w8a8_gemm), the single launch (fp8_linear_single_launch, the
+    quantisation fused into the GEMM) and fp8_linear itself, which takes the
+    single launch up to 16 rows and the chain above."""
     import torch
 
     import synth
@@ -251,11 +252,21 @@ def bench_decode_layer(Ms=(9, 16, 32), n_buffers=40, reps=5):
         x = _bf16_dev(synth.dense_workload(M=M, K=K, N=N, seed=1)["x"])
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(int(w8.lib().fp8_linear_workspace_bytes(M, K)), dtype=torch.uint8, device="cuda")
+        xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+
+        def chain(j):
+            def run():
+                w8.quantize_per_token(x, xq, xs)
+                w8.w8a8_gemm(xq, xs, wqs[j], wss[j], out=y)
+            return run
+
         rec = {}
         for name, mk in (
-            ("two_launch_us", lambda j: (lambda: w8.fp8_linear(x, wqs[j], wss[j], fast_math=True, out=y,
-                                                               workspace=ws))),
+            ("two_launch_us", chain),
             ("single_launch_us", lambda j: (lambda: w8.fp8_linear_single_launch(x, wqs[j], wss[j], out=y))),
+            ("fp8_linear_us", lambda j: (lambda: w8.fp8_linear(x, wqs[j], wss[j], fast_math=True, out=y,
+                                                               workspace=ws))),
         ):
             launches = [mk(j) for j in range(n_buffers)]
             for f in launches:

@@ -144,7 +144,9 @@ size_t fp8_linear_workspace_bytes(int64_t M, int64_t K);
 /*
  * fp8_linear — the layer as the model page's runtime chooses it: with
  * fast_math != 0 and more than 8 tokens (M > 8), quantize_per_token into the
- * workspace followed by w8a8_gemm; otherwise w8a16_gemm. The page states that
+ * workspace followed by w8a8_gemm (for M <= 16 and K <= 2048 as the single
+ * launch of fp8_linear_single_launch, which gives the same bits); otherwise
+ * w8a16_gemm. The page states that
  * the flag changes only steps that handle many tokens at once (prompt reading,
  * more than 8 conversations) and that a single conversation's generation uses
  * the default maths either way (Lernex/Metis-1.6-Logos-FP8, "What --fast-math

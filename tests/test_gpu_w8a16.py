@@ -83,11 +83,15 @@ def test_w8a16_every_code_single_product_exact(M):
     assert np.array_equal(got, want)
 
 
-def test_fp8_linear_dispatch():
-    d = synth.dense_workload(M=64, N=1024, K=1024, n_outlier=8, seed=3)
+@pytest.mark.parametrize("K", [1024, 4096])
+def test_fp8_linear_dispatch(K):
+    # M > 8 with fast maths: the FP8 chain, as one fused launch for M <= 16 and K <= 2048 and as
+    # quantisation + GEMM otherwise; both must give the bits of quantize_per_token + w8a8_gemm
+    d = synth.dense_workload(M=64, N=1040, K=K, n_outlier=8, seed=3)
     qw, sw = _weights(d)
     wq, ws = to_dev(qw), to_dev(sw)
-    for M in (64, 9, 8, 1):
+    for M in (64, 32, 17, 16, 12, 9, 8, 1):
+        print(f"[fp8_linear dispatch] M={M} K={K}", flush=True)
         x = to_dev_bf16(d["x"][:M])
         fast = bf16_bits(w8.fp8_linear(x, wq, ws, fast_math=True))
         slow = bf16_bits(w8.fp8_linear(x, wq, ws, fast_math=False))

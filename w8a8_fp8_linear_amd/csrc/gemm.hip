@@ -273,24 +273,26 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
 }
 
 // Fused decode: X BF16 [M, K] with M <= 16 * MT and K <= 512 * U (one round).
-template <int MT, int U>
+// NT tiles of 16 weight rows per workgroup share its quantised input, so
+// two tiles halve both the input re-reads and the quantisation work per
+// weight row.
+template <int MT, int U, int NT = 1>
 __global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W,
                                                      const float* __restrict__ sw, uint16_t* __restrict__ Y, int M,
                                                      int N, int K) {
-  __shared__ v4f red[3][MT][64];
+  __shared__ v4f red[3][NT][MT][64];
   __shared__ uint32_t wmax[4][MT * 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NT;
   const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K);
   const auto rX = make_rsrc(X, (int64_t)M * K * 2);
   const int r16 = lane & 15, g = lane >> 4;
-  const uint32_t wrow = (uint32_t)r16 * (uint32_t)K;
   const int nk = (K + 127) >> 7;
   // Weights first (their latency is the longest), then this wave's BF16
   // chunks: for K slice kt = wave + 4u, elements [128 kt + 16 g, +16) and
   // [128 kt + 64 + 16 g, +16) of each row, 32 bytes each.
-  v8i wf[U];
+  v8i wf[U][NT];
   uint4 xb[U][MT][4];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -299,9 +301,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict_
     const bool live = wave + 4 * u < nk;
     const uint32_t o0 = (live && c0 < K) ? (uint32_t)c0 : kOutOfRange;
     const uint32_t o1 = (live && c1 < K) ? (uint32_t)c1 : kOutOfRange;
-    const v4i lo = buffer_load16(rW, o0 == kOutOfRange ? o0 : wrow + o0);
-    const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
-    wf[u] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const uint32_t wrow = (uint32_t)(i * 16 + r16) * (uint32_t)K;
+      const v4i lo = buffer_load16(rW, o0 == kOutOfRange ? o0 : wrow + o0);
+      const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
+      wf[u][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const uint32_t xrow = (uint32_t)(t * 16 + r16) * (uint32_t)K * 2u;
@@ -337,9 +343,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict_
     s[t] = row_scale(a);
     r[t] = 1.0f / s[t];
   }
-  v4f acc[MT];
+  v4f acc[NT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -347,25 +355,31 @@ __global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict_
       const uint2 q0 = quant8(xb[u][t][0], s[t], r[t]), q1 = quant8(xb[u][t][1], s[t], r[t]);
       const uint2 q2 = quant8(xb[u][t][2], s[t], r[t]), q3 = quant8(xb[u][t][3], s[t], r[t]);
       const v8i xf = v8i{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, (int)q3.x, (int)q3.y};
-      acc[t] = mfma_16x16x128_e4m3(wf[u], xf, acc[t]);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i][t] = mfma_16x16x128_e4m3(wf[u][i], xf, acc[i][t]);
     }
   if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[wave - 1][t][lane] = acc[t];
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) red[wave - 1][i][t][lane] = acc[i][t];
   }
   __syncthreads();
   if (wave != 0) return;
-  const int n = n0 + 4 * g;
-  if (n >= N) return;
-  const float4 sW = *reinterpret_cast<const float4*>(sw + n);
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
-    const int m = t * 16 + r16;
-    if (m < M) {
-      const uint32_t p0 = bf16x2_rne(a[0] * s[t] * sW.x, a[1] * s[t] * sW.y);
-      const uint32_t p1 = bf16x2_rne(a[2] * s[t] * sW.z, a[3] * s[t] * sW.w);
-      *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
+  for (int i = 0; i < NT; ++i) {
+    const int n = n0 + i * 16 + 4 * g;
+    if (n >= N) continue;
+    const float4 sW = *reinterpret_cast<const float4*>(sw + n);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const v4f a = acc[i][t] + red[0][i][t][lane] + red[1][i][t][lane] + red[2][i][t][lane];
+      const int m = t * 16 + r16;
+      if (m < M) {
+        const uint32_t p0 = bf16x2_rne(a[0] * s[t] * sW.x, a[1] * s[t] * sW.y);
+        const uint32_t p1 = bf16x2_rne(a[2] * s[t] * sW.z, a[3] * s[t] * sW.w);
+        *reinterpret_cast<uint2*>(Y + (int64_t)m * N + n) = make_uint2(p0, p1);
+      }
     }
   }
 }
@@ -400,11 +414,11 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
 hipError_t launch_quant_gemm_decode(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
                                     int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const dim3 grid((unsigned)((N + 15) / 16));
+  const dim3 grid((unsigned)((N + 31) / 32));
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_skinny_q<1, 4>), grid, dim3(256), 0, stream, x, w, sw, y, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL((gemm_skinny_q<1, 4, 2>), grid, dim3(256), 0, stream, x, w, sw, y, (int)M, (int)N, (int)K);
   else
-    hipLaunchKernelGGL((gemm_skinny_q<2, 4>), grid, dim3(256), 0, stream, x, w, sw, y, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL((gemm_skinny_q<2, 4, 2>), grid, dim3(256), 0, stream, x, w, sw, y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
