@@ -30,9 +30,8 @@ What it defines, and where the pages state it:
 * The routed-expert chain (``moe``): routed experts in FP8 with the same
   scheme, top-k routing, the stack run twice with shared weights
   (Lernex/Metis-1.6-Praxis, "Architecture"; sglang-metis 0.1.0, "How the
-  model maps onto SGLang"); each routed copy's output in BF16 before the
-  top-k sum, as in the fused-MoE kernels the model is built on
-  (sglang-metis 0.1.0, the package description).
+  model maps onto SGLang"); a token's output is the router-weighted sum of
+  its routed copies' outputs at full precision, rounded once to BF16.
 
 Floating point is carried in float64; where a step is defined at float32
 precision (the scale and the scaled value fed to the E4M3 encoder) the
@@ -44,7 +43,7 @@ from .e4m3 import (E4M3_MAX, decode, decode_table, encode, encode_bits,
 from .bf16 import bf16_bits_to_f64, round_to_bf16_bits
 from .quant import bf16_bits_to_f32, quantize_rows
 from .linear import w8a8_linear, w8a8_linear_int, w8a16_linear
-from .moe import (route, grouped_gate_up, moe_pass, moe_two_pass, swiglu_f32, bf16_values)
+from .moe import (route, grouped_gate_up, moe_pass, moe_two_pass, swiglu_f32, bf16_values, combine_copies)
 from .mxfp4 import (e2m1_decode, e2m1_encode, e8m0_value, mx_dequant, mx_quantize_rows, mx_unpack, mxfp4_linear,
                     moe_mxfp4_pass, moe_mxfp4_two_pass)
 
@@ -52,6 +51,6 @@ __all__ = [
     "E4M3_MAX", "decode", "decode_table", "encode", "encode_bits", "finite_codes", "magnitudes",
     "bf16_bits_to_f64", "round_to_bf16_bits", "bf16_bits_to_f32", "quantize_rows",
     "w8a8_linear", "w8a8_linear_int", "w8a16_linear", "route", "grouped_gate_up", "moe_pass", "moe_two_pass",
-    "swiglu_f32", "bf16_values", "e2m1_decode", "e2m1_encode", "e8m0_value", "mx_dequant", "mx_quantize_rows", "mx_unpack",
+    "swiglu_f32", "bf16_values", "combine_copies", "e2m1_decode", "e2m1_encode", "e8m0_value", "mx_dequant", "mx_quantize_rows", "mx_unpack",
     "mxfp4_linear", "moe_mxfp4_pass", "moe_mxfp4_two_pass",
 ]

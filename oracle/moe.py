@@ -20,13 +20,14 @@ design notes):
 * Each token is quantised once over H; its k routed copies share that
   scale. h is rounded to float32 (not BF16) and requantised per routed
   copy (slot) with the same per-row quantiser.
-* The down projection W2[e] is [H, I]; each slot's output, scaled by its
-  router weight, is rounded to BF16 before the top-k sum, the model's dtype
-  between the expert stage and the sum as in the fused-MoE kernels the
-  model is built on (sglang-metis 0.1.0, the package description and
-  "Limitations"); the k BF16 outputs of a token are summed (exactly, in
-  float64 here) and rounded once to BF16. Router weights are inputs and are
-  not renormalised here.
+* The down projection W2[e] is [H, I]. A token's output is the router-
+  weighted sum of its k routed copies' outputs, taken at full precision and
+  rounded once to BF16 (the model's dtype): out[t] = bf16(sum_j w[t,j] *
+  y[t,j]). No page puts a rounding between the expert stage and that sum,
+  so none is placed there. The copies are added in the fixed order
+  j = 0, 1, ..., k-1, which makes the float64 sum independent of expert
+  labels and of the sorted order. Router weights are inputs and are not
+  renormalised here.
 * Slots are the flat indices t*k + j. The expert-sorted order is a stable
   sort of the slots by expert id; ids outside [0, E) are dropped and
   contribute nothing.
@@ -39,7 +40,8 @@ from .bf16 import bf16_bits_to_f64, round_to_bf16_bits
 from .linear import dequant_sum
 from .quant import quantize_rows
 
-__all__ = ["route", "grouped_gate_up", "swiglu_f32", "bf16_values", "moe_pass", "moe_two_pass"]
+__all__ = ["route", "grouped_gate_up", "swiglu_f32", "bf16_values", "combine_copies", "moe_pass",
+           "moe_two_pass"]
 
 
 def route(ids, E: int):
@@ -96,6 +98,16 @@ def bf16_values(y) -> np.ndarray:
     return bf16_bits_to_f64(round_to_bf16_bits(y))
 
 
+def combine_copies(wy) -> np.ndarray:
+    """sum_j wy[:, j, :] over the top-k positions in the order j = 0, 1, ...
+    (float64; a dropped slot's row is zero)."""
+    wy = np.asarray(wy, dtype=np.float64)
+    out = wy[:, 0, :].copy()
+    for j in range(1, wy.shape[1]):
+        out += wy[:, j, :]
+    return out
+
+
 def moe_pass(qx, sx, ids, w, qw13, s13, qw2, s2, keep=False):
     """One routed-expert pass on quantised tokens.
 
@@ -112,9 +124,10 @@ def moe_pass(qx, sx, ids, w, qw13, s13, qw2, s2, keep=False):
     gu, perm = grouped_gate_up(qx, sx, ids, qw13, s13)
     h = swiglu_f32(gu)
     qh, sh, vh = quantize_rows(h)
-    out = np.zeros((T, H), dtype=np.float64)
     _, offsets, _ = route(ids, E)
     flat_e = np.asarray(ids).reshape(-1)
+    # the weighted product of every routed copy, in float64, on its slot's row
+    wy = np.zeros((T * k, H), dtype=np.float64)
     for e in range(E):
         lo, hi = offsets[e], offsets[e + 1]
         if lo == hi:
@@ -124,7 +137,8 @@ def moe_pass(qx, sx, ids, w, qw13, s13, qw2, s2, keep=False):
         acc = dequant_sum(qh[lo:hi], qw2[e])
         y = (sh[lo:hi].astype(np.float64)[:, None] *
              np.asarray(s2[e], np.float32).astype(np.float64)[None, :]) * acc
-        np.add.at(out, slots // k, bf16_values(w[slots][:, None] * y))
+        wy[slots] = w[slots][:, None] * y
+    out = combine_copies(wy.reshape(T, k, H))
     extra = None
     if keep:
         extra = {"gu": gu, "h": h, "qh": qh, "sh": sh, "vh": vh, "perm": perm}

@@ -9,6 +9,10 @@
 * k routed copies of one expert whose weights sum to 1 give that expert's
   output; relabelling experts (ids and weight stacks together) and
   reordering tokens act as they must.
+* The combine rounds once: two copies of one expert with the weights 3/8
+  and 5/8 give the single copy's BF16 output bit for bit, where rounding
+  each weighted copy to BF16 before the sum would not (the test checks that
+  the data tells the two apart).
 * SiLU agrees with torch's silu in float64 (library routine).
 * The two-pass stack feeds each pass the previous pass's BF16 output.
 """
@@ -77,7 +81,7 @@ def test_single_expert_reduces_to_dense_chain():
     y, ybf = oracle.w8a8_linear(qh, sh, d["q2"][0], d["s2"][0])
     assert np.array_equal(extra["perm"], np.arange(T))
     assert np.array_equal(extra["qh"], qh) and np.array_equal(extra["sh"], sh)
-    assert np.array_equal(out64, oracle.bf16_bits_to_f64(ybf)) and np.array_equal(out_bf, ybf)
+    assert np.array_equal(out64, y) and np.array_equal(out_bf, ybf)
 
 
 def test_k_copies_of_one_expert_weights_summing_to_one():
@@ -91,12 +95,44 @@ def test_k_copies_of_one_expert_weights_summing_to_one():
     w2 = np.full((T, 2), 0.5, np.float32)
     out, out_bf, _ = oracle.moe_pass(d["qx"], d["sx"], ids2, w2, d["q13"], d["s13"], d["q2"], d["s2"])
     assert np.array_equal(out, base) and np.array_equal(out_bf, base_bf)
-    # four copies with power-of-two weights: each BF16 copy is an exact
-    # fraction of the single copy, so the sum is exact too
+    # four copies with power-of-two weights: each weighted copy is an exact
+    # fraction of the single copy; their float64 sum is the single copy up
+    # to float64 rounding, and rounds to the same BF16
     ids4 = np.full((T, 4), 2, np.int32)
     w4 = np.tile(np.array([0.5, 0.25, 0.125, 0.125], np.float32), (T, 1))
-    out4, _, _ = oracle.moe_pass(d["qx"], d["sx"], ids4, w4, d["q13"], d["s13"], d["q2"], d["s2"])
-    assert np.array_equal(out4, base)
+    out4, out4_bf, _ = oracle.moe_pass(d["qx"], d["sx"], ids4, w4, d["q13"], d["s13"], d["q2"], d["s2"])
+    assert np.allclose(out4, base, rtol=2.0 ** -50, atol=0.0)
+    assert np.array_equal(out4_bf, base_bf)
+
+
+def _per_copy_reading(copies):
+    """The rejected reading of the combine, for contrast: each weighted copy
+    rounded to BF16 first, then the sum rounded once more."""
+    return oracle.round_to_bf16_bits(sum(oracle.bf16_values(c) for c in copies))
+
+
+def test_combine_rounds_the_exact_sum_once():
+    d = _small(seed=11, E=3, k=1, T=48, H=64)
+    T = d["x"].shape[0]
+    args = (d["q13"], d["s13"], d["q2"], d["s2"])
+    base, base_bf, _ = oracle.moe_pass(d["qx"], d["sx"], np.full((T, 1), 2, np.int32), np.ones((T, 1), np.float32),
+                                       *args)
+    w = np.tile(np.array([0.375, 0.625], np.float32), (T, 1))
+    out, out_bf, _ = oracle.moe_pass(d["qx"], d["sx"], np.full((T, 2), 2, np.int32), w, *args)
+    # 3/8 y + 5/8 y is y up to float64 rounding, and y rounds to the same BF16
+    assert np.allclose(out, base, rtol=2.0 ** -50, atol=0.0)
+    assert np.array_equal(out_bf, base_bf)
+    # the per-copy reading gives other bits on this data: the pin tells them apart
+    other = _per_copy_reading([0.375 * base, 0.625 * base])
+    assert (other != base_bf).sum() > T
+    # three copies with weights that do not sum to a power of two: one
+    # rounding of the float64 sum, taken in the order j = 0, 1, 2
+    w3 = np.tile(np.array([0.3, 0.45, 0.2], np.float32), (T, 1))
+    out3, out3_bf, _ = oracle.moe_pass(d["qx"], d["sx"], np.full((T, 3), 2, np.int32), w3, *args)
+    wv = w3[0].astype(np.float64)
+    want = (wv[0] * base + wv[1] * base) + wv[2] * base
+    assert np.array_equal(out3, want)
+    assert np.array_equal(out3_bf, oracle.round_to_bf16_bits(want))
 
 
 def test_relabelled_experts_and_reordered_tokens():
@@ -108,7 +144,7 @@ def test_relabelled_experts_and_reordered_tokens():
     inv = np.argsort(relabel)                                      # new id -> old id
     out2, _, _ = oracle.moe_pass(d["qx"], d["sx"], relabel[d["ids"]], d["w"],
                                  d["q13"][inv], d["s13"][inv], d["q2"][inv], d["s2"][inv])
-    # the k BF16 terms of a token are summed in another order: exact in float64
+    # the k copies of a token are added in the same j order: identical sums
     assert np.array_equal(out2, out)
     order = np.random.default_rng(6).permutation(d["qx"].shape[0])
     out3, _, _ = oracle.moe_pass(d["qx"][order], d["sx"][order], d["ids"][order], d["w"][order], *args)

@@ -216,7 +216,7 @@ def test_moe_single_expert_reduces_to_dense_chain():
     y, ybf = oracle.mxfp4_linear(qh, sh, d["q2"][0], d["s2"][0])
     assert np.array_equal(extra["perm"], np.arange(T))
     assert np.array_equal(extra["qh"], qh) and np.array_equal(extra["sh"], sh)
-    assert np.array_equal(out64, oracle.bf16_bits_to_f64(ybf)) and np.array_equal(out_bf, ybf)
+    assert np.array_equal(out64, y) and np.array_equal(out_bf, ybf)
 
 
 def test_moe_split_weights_relabelling_and_dropped_ids():
@@ -240,6 +240,21 @@ def test_moe_split_weights_relabelling_and_dropped_ids():
     dropped, _, _ = oracle.moe_mxfp4_pass(d["x"], ids, d["w"], *_weights(d))
     zeroed, _, _ = oracle.moe_mxfp4_pass(d["x"], d["ids"], w0, *_weights(d))
     assert np.array_equal(dropped, zeroed)
+
+
+def test_moe_combine_rounds_the_exact_sum_once():
+    """Two copies of one expert with the weights 3/8 and 5/8 give the single
+    copy's BF16 output; rounding each weighted copy to BF16 first would not."""
+    d = _small(seed=12, T=40)
+    T = d["x"].shape[0]
+    base, base_bf, _ = oracle.moe_mxfp4_pass(d["x"], np.full((T, 1), 1, np.int32), np.ones((T, 1), np.float32),
+                                             *_weights(d))
+    w = np.tile(np.array([0.375, 0.625], np.float32), (T, 1))
+    out, out_bf, _ = oracle.moe_mxfp4_pass(d["x"], np.full((T, 2), 1, np.int32), w, *_weights(d))
+    assert np.allclose(out, base, rtol=2.0 ** -50, atol=0.0)
+    assert np.array_equal(out_bf, base_bf)
+    per_copy = oracle.round_to_bf16_bits(oracle.bf16_values(0.375 * base) + oracle.bf16_values(0.625 * base))
+    assert (per_copy != base_bf).sum() > T
 
 
 def test_moe_two_pass_chains_bf16_outputs():
