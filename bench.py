@@ -500,7 +500,7 @@ def bench_moe_two_pass(reps=5, warmup=2):
                         device="cuda")
     hq, hs = w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0, workspace=gu_ws)
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
     for name, fn, fl in (
         ("gate_up_swiglu_quant", lambda: w8.moe_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0,
                                                                      workspace=gu_ws),
@@ -607,7 +607,7 @@ def bench_moe_mxfp4(reps=10, warmup=3):
             _, off0, perm0 = w8.moe_route(ids, E, order=0)
             hq, hs = w8.moe_mxfp4_gate_up_swiglu_quant(xq, xs, perm0, off0, q13, s13, k, order=0)
             o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-            y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+            y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
             stages = {}
             for name, fn, fl in (
                 ("quantize", lambda: w8.mxfp4_quantize(x, xq, xs), 0),

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define W8A8_ABI_VERSION 1
+#define W8A8_ABI_VERSION 2
 
 enum {
   W8A8_OK = 0,
@@ -113,6 +113,26 @@ int quantize_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, uint8_t* q_
 int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
               uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+
+/*
+ * e4m3_from_f32, bf16_from_f32 — the final conversions of this library on
+ * caller-given float32 values, for checking them on the device.
+ *
+ * Every FP8 byte the quantisers write is the E4M3 code of a float32 scaled
+ * value (the OCP E4M3FN format the checkpoints store, Lernex/Metis-1.6-
+ * Logos-FP8, "What is in FP8"), and every BF16 result is a float32 value
+ * rounded to the model's dtype (same page, "What --fast-math does"). These
+ * two calls run exactly those device steps:
+ *   q_e4m3[i] = E4M3(clamp(v[i], -448, 448))   round to nearest even, the
+ *               sign kept on a zero result
+ *   y_bf16[i] = BF16(v[i])                     round to nearest even
+ *   v          [n] float32 input (read only); NaN gives an unspecified code
+ *   q_e4m3 / y_bf16  [n] output
+ * Errors: NULL_ARG, BAD_SHAPE (n < 0), UNSUPPORTED (n > 2^40), MISALIGNED,
+ *         DEVICE, LAUNCH.
+ */
+int e4m3_from_f32(const float* v, int64_t n, uint8_t* q_e4m3, hipStream_t stream);
+int bf16_from_f32(const float* v, int64_t n, uint16_t* y_bf16, hipStream_t stream);
 
 /*
  * w8a16_gemm — the default maths: BF16 activations times the E4M3 weights
@@ -260,27 +280,34 @@ size_t moe_gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t to
  * slot_row array of moe_route in the other order: the tiles then follow
  * `perm`, the output rows the other order). Rows from offsets[G] on are left
  * untouched. I must be a multiple of 128. `order` is the order perm/offsets
- * were made with. The workspace holds the float32 h rows and their maxima.
+ * were made with. The workspace holds the row maxima and, unless h_f32 is
+ * given, the float32 h rows.
+ *   h_f32 [T*topk, I]  optional (NULL: not written): the float32 h rows the
+ *                      codes were made from, in the same rows as h_q, so that
+ *                      a caller can check the requantisation bit for bit.
  */
 int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
                              const int32_t* dst_row, const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q,
-                             float* h_scale, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+                             float* h_scale, float* h_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                             int order, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_down_combine — grouped down projection and router-weighted combine:
- *   y[slot, :]   = bf16( topk_w[slot] * h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T) )
+ *   y[slot, :]   = topk_w[slot] * h_scale[r] * w2_scale[e, :] * (h_q[r, :] . w2_q[e]^T)
  *                  for the slot of sorted row r (product and scaling in float32)
  *   out_bf16[t]  = bf16( sum over j = 0..topk-1 with a valid id of y[t*topk + j] )
- * The sum is float32 and always taken in the order j = 0, 1, ... (so the
- * result does not depend on the sorted order and is deterministic).
- * perm/offsets may be in either order (`order`); topk_ids tells the valid
- * slots. y_bf16 [T*topk, H] is caller-provided BF16 scratch. A token with
- * no valid slot gets zeros.
+ * Each routed copy is kept in float32; the sum is float32, always taken in
+ * the order j = 0, 1, ... (so the result does not depend on the sorted
+ * order and is deterministic), and rounded to BF16 once. No page puts a
+ * rounding between the experts and the top-k sum (Lernex/Metis-1.6-Logos-
+ * FP8, "What is in FP8"; sglang-metis 0.1.0, "How the model maps onto
+ * SGLang"). perm/offsets may be in either order (`order`); topk_ids tells
+ * the valid slots. y_f32 [T*topk, H] is caller-provided float32 scratch. A
+ * token with no valid slot gets zeros.
  */
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
                      const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const float* w2_scale,
-                     uint16_t* out_bf16, uint16_t* y_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     uint16_t* out_bf16, float* y_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                      int order, hipStream_t stream);
 
 /* Bytes of scratch w8a8_grouped_gemm needs (0 for invalid sizes). */
@@ -387,17 +414,17 @@ int moe_mxfp4_gate_up_swiglu_quant(const uint8_t* x_q, const uint8_t* x_scale, c
 
 /*
  * moe_mxfp4_down_combine — grouped down projection and combine:
- *   y[slot, :]  = bf16( topk_w[slot] * (h[r] . W2[e]^T) )   (sorted row r)
+ *   y[slot, :]  = topk_w[slot] * (h[r] . W2[e]^T)            (sorted row r, float32)
  *   out_bf16[t] = bf16( sum over valid j, in order j = 0, 1, ... of y[t*topk + j] )
- *                 (float32 sum)
- *   y_bf16 [T*topk, H] is caller-provided BF16 scratch.
+ *                 (float32 sum, one rounding)
+ *   y_f32 [T*topk, H] is caller-provided float32 scratch.
  *   out_q [T, H/2], out_scale [T, H/32]  optional (both NULL or both set):
  *               mxfp4_quantize(out_bf16), bit for bit, fused into the
  *               combine — the next pass's expert input.
  */
 int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int32_t* perm, const int32_t* offsets,
                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const uint8_t* w2_scale,
-                           uint16_t* out_bf16, uint16_t* y_bf16, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
+                           uint16_t* out_bf16, float* y_f32, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
                            int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
 /* Bytes of scratch moe_mxfp4_grouped needs (0 for invalid sizes). */

@@ -10,7 +10,7 @@ import numpy as np
 
 import oracle
 import synth
-from gpu_util import MFMA_GROUP_ERR, U32, bf16_ulp
+from gpu_util import MFMA_GROUP_ERR, U32, bf16_ulp, map_row_chunks
 
 SILU_DERIV_MAX = 1.1  # max |d silu / dg| over the reals is ~1.0998
 
@@ -29,13 +29,10 @@ def quantized_moe(T, H, I, E, k, n_outlier=0, passes=1, seed=0):
     }
 
 
-def _quant_rows_chunked(x, rows=16384):
-    qs, ss = [], []
-    for i in range(0, x.shape[0], rows):
-        q, s, _ = oracle.quantize_rows(x[i:i + rows])
-        qs.append(q)
-        ss.append(s)
-    return np.concatenate(qs), np.concatenate(ss)
+def _quant_rows_chunked(x, rows=8192):
+    """oracle.quantize_rows over row chunks (chunks on a thread pool)."""
+    res = map_row_chunks(oracle.quantize_rows, x, rows)
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
 
 
 def sorted_rows_gate_up(qx, sx, ids, perm, rows, q13, s13, k):
@@ -110,11 +107,11 @@ def check_requant(qh_gpu, sh_gpu, gu64, gu_err):
 def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
     """Oracle down projection + combine for ``tokens``, from sorted h codes.
 
-    Each routed copy's output is rounded to BF16 and the copies are summed
-    exactly. Returns (out64 [n, H], err [n, H]); err bounds |out_gpu - out64|
-    before the final BF16 rounding: per copy the E4M3 matrix-core bound plus
-    one BF16 ulp (the GPU rounds its float32 value, which may sit on the other
-    side of a rounding midpoint), then the float32 sum.
+    The router-weighted copies are summed at full precision (the value the
+    GPU rounds once to BF16). Returns (out64 [n, H], err [n, H]); err bounds
+    |out_gpu - out64| before the final BF16 rounding: per copy the E4M3
+    matrix-core bound and the float32 scalings, then the float32 rounding of
+    each stored copy and of the float32 sum.
     """
     tokens = np.asarray(tokens)
     E, H, I = q2.shape
@@ -138,9 +135,9 @@ def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
             scale = (sh[rows[sel]].astype(np.float64) * w[slots[sel]])[:, None] * s2[e].astype(np.float64)[None, :]
             y = scale * (a @ b.T)
             ey = (MFMA_GROUP_ERR + (I / 128 + 4) * U32) * 1.01 * scale * (np.abs(a) @ np.abs(b).T)
-            out[sel] += oracle.bf16_values(y)
+            out[sel] += y
             absout[sel] += np.abs(y)
-            err[sel] += ey + bf16_ulp(np.abs(y) + ey)
+            err[sel] += ey
     err += (k + 2) * U32 * 1.01 * absout
     return out, err
 

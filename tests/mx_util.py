@@ -10,18 +10,15 @@ import numpy as np
 
 import oracle
 import synth
-from gpu_util import MFMA_GROUP_ERR, U32, bf16_ulp
+from gpu_util import MFMA_GROUP_ERR, U32, map_row_chunks
 from moe_util import swiglu_bound
 
 
 def mx_quantize_chunked(x, rows=2048):
-    """oracle.mx_quantize_rows over row chunks (bounded temporary memory)."""
-    qs, ss = [], []
-    for i in range(0, x.shape[0], rows):
-        q, s = oracle.mx_quantize_rows(x[i:i + rows])
-        qs.append(q)
-        ss.append(s)
-    return np.concatenate(qs), np.concatenate(ss)
+    """oracle.mx_quantize_rows over row chunks (bounded temporary memory, chunks
+    on a thread pool)."""
+    res = map_row_chunks(oracle.mx_quantize_rows, x, rows)
+    return np.concatenate([q for q, _ in res]), np.concatenate([s for _, s in res])
 
 
 def quantized_mx_moe(T, H, I, E, k, n_outlier=0, passes=1, seed=0):
@@ -114,8 +111,10 @@ def check_mx_requant(qh_gpu, sh_gpu, gu64, gu_err):
 
 def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
     """Exact down projection + combine for ``tokens`` from sorted MXFP4 h rows
-    (each routed copy's output rounded to BF16, the copies summed exactly),
-    and a bound on |out_gpu - out64| before the final BF16 rounding."""
+    (the router-weighted copies summed at full precision, the value the GPU
+    rounds once to BF16), and a bound on |out_gpu - out64| before that
+    rounding: per copy the FP4 matrix-core bound, then the float32 rounding
+    of each stored copy and of the float32 sum."""
     tokens = np.asarray(tokens)
     E, H, _ = q2.shape
     I = 2 * q2.shape[2]
@@ -139,8 +138,8 @@ def down_combine_ref(qh, sh, perm, ids, tw, q2, s2, k, tokens):
             wt = w[slots[sel]][:, None]
             y = wt * (a @ b.T)
             ey = np.abs(wt) * mx_bound(a, b, I)
-            out[sel] += oracle.bf16_values(y)
+            out[sel] += y
             absout[sel] += np.abs(y)
-            err[sel] += ey + bf16_ulp(np.abs(y) + ey)
+            err[sel] += ey
     err += (k + 2) * U32 * 1.01 * absout
     return out, err

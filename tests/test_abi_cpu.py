@@ -39,7 +39,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert w8.abi_version() == 1
+    assert w8.abi_version() == 2
     for s in range(8):
         assert w8.lib().w8a8_status_string(s)
     assert w8.lib().w8a8_status_string(99) == b"unknown status"
@@ -156,3 +156,24 @@ def test_mxfp4_expert_argument_errors():
     import torch
     if not torch.cuda.is_available():
         assert g(*([P] * 9), None, None, T, H, I, E, k, P, need, None) == DEV
+
+
+def test_conversion_argument_errors():
+    for name in ("e4m3_from_f32", "bf16_from_f32"):
+        f = getattr(w8.lib(), name)
+        assert f(P, -1, P, None) == SHAPE
+        assert f(P, (1 << 40) + 1, P, None) == UNSUP
+        assert f(P, 0, P, None) == OK              # empty: no-op, no device needed
+        assert f(None, 4, P, None) == NULL
+        assert f(P, 4, None, None) == NULL
+        assert f(P + 4, 4, P, None) == MIS
+        assert f(P, 4, P + 2, None) == MIS
+        assert f(P, 4, P, None) == DEV             # valid arguments: no GPU here
+
+
+def test_gate_up_swiglu_quant_h_output_alignment():
+    f = w8.lib().moe_gate_up_swiglu_quant
+    args = [P] * 9 + [P + 4]                       # h_f32 misaligned
+    assert f(*args, 8, 256, 128, 2, 2, 0, P, 1 << 30, None) == MIS
+    args[9] = None                                  # h_f32 is optional
+    assert f(*args, 8, 256, 128, 2, 2, 0, P, 1 << 30, None) == DEV

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import bf16_bits, gemm_report, record, to_dev, to_dev_bf16, w8a16_report
+from gpu_util import MAX_ABS_GUARD, bf16_bits, gemm_report, record, to_dev, to_dev_bf16, w8a16_report
 
 pytestmark = pytest.mark.gpu
 
@@ -174,11 +174,24 @@ def test_gemm_prefill_full_size():
     record("gemm prefill 4096x2048->6144 (full)", rep)
     assert rep["n_bound_violations"] == 0, rep
     assert rep["frobenius"] <= 4e-3, rep
-    # The literal max-abs criterion (1e-2 * rms) is reported, not asserted:
-    # BF16 one-ulp flips alone exceed it wherever |y| > 2.56 rms, and the
-    # E4M3 MFMA's 14-bit group alignment adds more (about 0.03 rms at most
-    # here, on 0.012% of the elements). Guard against regressions instead.
-    assert rep["max_abs_over_rms"] <= 0.06, rep
+    # The literal max-abs criterion (1e-2 * rms) is reported with its count;
+    # the largest difference is guarded (see gpu_util.MAX_ABS_GUARD).
+    assert rep["max_abs_over_rms"] <= MAX_ABS_GUARD, rep
+
+
+def test_gemm_small_workload():
+    """The 64 x 1024 -> 1024 workload (seed 0, 8 outlier channels), every
+    element, against the bound; the literal max-abs criterion reported."""
+    d = synth.dense_workload(**synth.DENSE_SMALL, seed=0)
+    qx, sx, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["x"]))
+    qw, sw, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["w"]))
+    got = _run_gemm(qx, sx, qw, sw)
+    rep = gemm_report(got, qx, sx, qw, sw)
+    print("small workload", rep, flush=True)
+    record("gemm small workload 64x1024->1024 (seed 0)", rep)
+    assert rep["n_bound_violations"] == 0, rep
+    assert rep["frobenius"] <= 4e-3, rep
+    assert rep["max_abs_over_rms"] <= MAX_ABS_GUARD, rep
 
 
 def test_gemm_invariants():

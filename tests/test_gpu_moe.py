@@ -5,10 +5,17 @@
 * Fused SwiGLU + requantisation: scales within the propagated bound and
   every code explainable (differs from the oracle's only where the oracle's
   scaled value lies within the propagated error of a rounding boundary).
+* The requantisation on the GPU's own float32 h rows: codes and scales equal
+  the oracle's quantiser bit for bit (small shapes, the 4096-token workload,
+  a 256 x 256-tile shape), and h within its propagated bound.
 * Down + combine: fed the GPU's own requantised rows, every output element
-  of the sampled tokens inside the bound.
-* Full pass and the two-pass stack: normalised Frobenius <= 4e-3 against the
-  oracle, pass 2 teacher-forced with the GPU's pass-1 output.
+  of the sampled tokens inside the bound (the weighted copies summed at full
+  precision and rounded once).
+* Full pass: normalised Frobenius <= 4e-3 against the oracle. The two-pass
+  stack: the benched entry point equals the stage-by-stage chain bit for
+  bit, every stage is checked element by element on its own GPU input, and
+  each pass end to end within Frobenius 4e-3 (pass 2 from the GPU's pass-1
+  output).
 Shapes: the routed-expert workloads (4096 and 16384 tokens, H 2048, I 512,
 64 experts, top-8, Zipf routing) and small ragged ones.
 """
@@ -18,7 +25,7 @@ import pytest
 import oracle
 from gpu_util import bf16_bits, record, to_dev
 from moe_util import (bf16_compare, check_requant, down_combine_ref, quantized_moe,
-                      sorted_rows_gate_up)
+                      sorted_rows_gate_up, swiglu_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -232,13 +239,15 @@ def test_down_combine_mid(mid):
     _check_down(mid, hq, hs, perm, offsets)
 
 
-# Groups of 512 rows or more (the 256 x 256 tiles) on shapes the workloads
-# above do not reach: a ragged N tail, 6 and 8 K steps in the down
-# projection, one n-tile, more tiles than CUs.
+# Groups of 1024 rows or more on average: the 256 x 256 tiles (smaller
+# averages run 128 x 128 or 64 x 128 tiles), on shapes the workloads above
+# do not reach: a ragged N tail, 6 and 8 K steps in the down projection, one
+# n-tile, more tiles than CUs.
+LARGE_TILE_MIN_ROWS = 1024
 LARGE_GROUPS = [
-    dict(T=1100, H=2064, I=512, E=2, k=1, n_outlier=3),   # an N tail: 2064 = 8 x 256 + 16
-    dict(T=700, H=512, I=1024, E=1, k=1, n_outlier=2),    # 8 K steps
-    dict(T=600, H=256, I=768, E=1, k=1, n_outlier=2),     # 6 K steps, one n-tile
+    dict(T=2200, H=2064, I=512, E=2, k=1, n_outlier=3),   # an N tail: 2064 = 8 x 256 + 16
+    dict(T=1100, H=512, I=1024, E=1, k=1, n_outlier=2),   # 8 K steps
+    dict(T=1100, H=256, I=768, E=1, k=1, n_outlier=2),    # 6 K steps, one n-tile
     dict(T=4096, H=2048, I=512, E=2, k=2, n_outlier=4),   # 272 tiles: more than one per workgroup
 ]
 
@@ -247,9 +256,57 @@ LARGE_GROUPS = [
 @pytest.mark.parametrize("order", [0, 1])
 def test_down_combine_large_groups(cfg, order):
     print(f"[large groups] {cfg} order={order}", flush=True)
+    groups = cfg["E"] * (cfg["k"] if order else 1)
+    assert cfg["T"] * cfg["k"] // groups >= LARGE_TILE_MIN_ROWS
     d = quantized_moe(**cfg, seed=17)
     hq, hs, perm, offsets = _check_fused_requant(d, tile_order=order, row_order=order, sample=2048)
     _check_down(d, hq, hs, perm, offsets, n_tokens=min(512, d["T"]), order=order)
+
+
+def _check_requant_bitexact(d, route_idx=0, sample=None):
+    """The fused gate/up + SwiGLU + requantisation, with the float32 h rows the
+    codes were made from: the codes and scales must equal the oracle's
+    quantiser on those h rows bit for bit, and h itself must lie within the
+    bound carried from the gate/up products."""
+    dv = _dev(d)
+    ids, _ = d["routes"][route_idx]
+    _, off, perm = w8.moe_route(to_dev(ids), d["E"])
+    hq, hs, h = w8.moe_gate_up_swiglu_quant(dv["qx"], dv["sx"], perm, off, dv["q13"], dv["s13"], d["k"],
+                                            return_h=True)
+    torch.cuda.synchronize()
+    _, _, rp = oracle.route(ids, d["E"])
+    rows = np.arange(rp.size) if sample is None else np.sort(
+        np.random.default_rng(4).choice(rp.size, min(sample, rp.size), replace=False))
+    h_gpu = h.cpu().numpy()[rows]
+    q_ref, s_ref, _ = oracle.quantize_rows(h_gpu)
+    q_gpu, s_gpu = hq.cpu().numpy()[rows], hs.cpu().numpy()[rows]
+    bad = np.argwhere(q_gpu != q_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ from the oracle's quantiser on the GPU's h, first {bad[:4].tolist()}"
+    assert np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32))
+    gu64, err = sorted_rows_gate_up(d["qx"], d["sx"], ids, rp, rows, d["q13"], d["s13"], d["k"])
+    h32, dh = swiglu_bound(gu64, err)
+    over = np.abs(h_gpu.astype(np.float64) - h32) > dh
+    assert not over.any(), f"{over.sum()} h values outside the propagated bound"
+    rep = {"rows": int(rows.size), "codes": int(q_ref.size), "max_h_err_over_bound":
+           float(np.max(np.abs(h_gpu - h32) / dh))}
+    print("requant bit-exact", rep, flush=True)
+    record(f"moe requant bit-exact on GPU h T={d['T']} E={d['E']} k={d['k']}", rep)
+
+
+@pytest.mark.parametrize("cfg", ["small", "ragged", "mid"])
+def test_requant_bitexact_small(cfg, request):
+    _check_requant_bitexact(request.getfixturevalue(cfg))
+
+
+def test_requant_bitexact_gate_up_cfg(gate_up_cfg):
+    """4096 tokens, top-8 of 64 experts: every routed slot's codes and scale."""
+    _check_requant_bitexact(gate_up_cfg)
+
+
+def test_requant_bitexact_large_groups():
+    """A 256 x 256-tile shape (2048 rows per group)."""
+    d = quantized_moe(**LARGE_GROUPS[3], seed=19)
+    _check_requant_bitexact(d, sample=4096)
 
 
 def test_down_combine_deterministic(small):
@@ -304,34 +361,75 @@ def test_full_pass_small(cfg, request):
 
 
 def test_two_pass_stack(two_pass_cfg):
-    """16384 tokens, two passes with the same weights; 384 sampled tokens per pass.
-    Pass 2 is teacher-forced: the oracle's pass 2 starts from the GPU's pass-1 output."""
+    """16384 tokens, two passes with the same weights, 512 sampled tokens per pass.
+
+    The benched path (moe_ffn: two moe_w8a8_grouped calls, the next pass's
+    input quantised in the first pass's combine) must equal the stage-by-stage
+    chain bit for bit; each stage of the chain is then checked element by
+    element, each fed the GPU's own input of that stage (teacher forcing):
+    the token codes bit-exact, h inside its propagated bound, the requantised
+    codes bit-exact on the GPU's h, the down projection + combine inside the
+    element bound. End to end, each pass is compared with the oracle's pass
+    from the GPU's own input (pass 2 starts from the GPU's pass-1 output)."""
     d = two_pass_cfg
     dv = _dev(d)
-    routes_dev = [(to_dev(i), to_dev(w)) for i, w in d["routes"]]
     from gpu_util import to_dev_bf16
     x = to_dev_bf16(d["x_bits"])
+    routes_dev = [(to_dev(i), to_dev(w)) for i, w in d["routes"]]
     ws = w8.moe_workspace(d["T"], d["H"], d["I"], d["E"], d["k"])
     outs = w8.moe_ffn(x, routes_dev, dv["q13"], dv["s13"], dv["q2"], dv["s2"], workspace=ws)
     torch.cuda.synchronize()
-    tokens = np.sort(np.random.default_rng(3).choice(d["T"], 384, replace=False))
-    # pass 1 from the oracle's own quantised input
-    ids1, w1 = d["routes"][0]
-    ref1 = _oracle_pass_tokens(d["qx"], d["sx"], ids1, w1, d, tokens)
-    p1_bits = bf16_bits(outs[0])
-    rep1 = bf16_compare(p1_bits[tokens], ref1)
-    print("pass 1", rep1, flush=True)
-    record("moe two-pass T=16384 pass 1 (384 tokens)", rep1)
-    assert rep1["frobenius"] <= 4e-3, rep1
-    # pass 2 from the GPU's pass-1 output (teacher forcing)
-    x2 = oracle.bf16_bits_to_f64(p1_bits[tokens]).astype(np.float32)
-    qx2, sx2, _ = oracle.quantize_rows(x2)
-    ids2, w2 = d["routes"][1]
-    ref2, _, _ = oracle.moe_pass(qx2, sx2, ids2[tokens], w2[tokens], d["q13"], d["s13"], d["q2"], d["s2"])
-    rep2 = bf16_compare(bf16_bits(outs[1])[tokens], ref2)
-    print("pass 2 (teacher-forced)", rep2, flush=True)
-    record("moe two-pass T=16384 pass 2 teacher-forced (384 tokens)", rep2)
-    assert rep2["frobenius"] <= 4e-3, rep2
+    tokens = np.sort(np.random.default_rng(3).choice(d["T"], 512, replace=False))
+    xq, xs = w8.quantize_per_token(x)
+    x_bits = d["x_bits"]
+    for p, ((ids, tw), (ids_d, tw_d)) in enumerate(zip(d["routes"], routes_dev)):
+        print(f"[two-pass] pass {p + 1}", flush=True)
+        # the token codes of this pass's input
+        qx_ref, sx_ref, _ = oracle.quantize_rows(oracle.bf16_bits_to_f64(x_bits).astype(np.float32))
+        assert np.array_equal(xq.cpu().numpy(), qx_ref) and np.array_equal(xs.cpu().numpy(), sx_ref)
+        _, off, perm = w8.moe_route(ids_d, d["E"])
+        hq, hs, h = w8.moe_gate_up_swiglu_quant(xq, xs, perm, off, dv["q13"], dv["s13"], d["k"], return_h=True)
+        out = w8.moe_down_combine(hq, hs, perm, off, ids_d, tw_d, dv["q2"], dv["s2"])
+        torch.cuda.synchronize()
+        out_bits = bf16_bits(out)
+        assert np.array_equal(out_bits, bf16_bits(outs[p])), "moe_ffn differs from the stage-by-stage chain"
+        # h and its requantisation on the sampled tokens' slots
+        _, _, rp = oracle.route(ids, d["E"])
+        inv = np.full(ids.size, -1, np.int64)
+        inv[rp] = np.arange(rp.size)
+        rows = np.sort(inv[(tokens[:, None] * d["k"] + np.arange(d["k"])[None, :]).reshape(-1)])
+        rows = rows[rows >= 0]
+        h_gpu = h.cpu().numpy()[rows]
+        q_ref, s_ref, _ = oracle.quantize_rows(h_gpu)
+        assert np.array_equal(hq.cpu().numpy()[rows], q_ref)
+        assert np.array_equal(hs.cpu().numpy()[rows].view(np.uint32), s_ref.view(np.uint32))
+        gu64, err = sorted_rows_gate_up(qx_ref, sx_ref, ids, rp, rows, d["q13"], d["s13"], d["k"])
+        h32, dh = swiglu_bound(gu64, err)
+        assert not (np.abs(h_gpu.astype(np.float64) - h32) > dh).any(), "h outside its bound"
+        rq = check_requant(hq.cpu().numpy()[rows], hs.cpu().numpy()[rows], gu64, err)
+        # down projection + combine from the GPU's codes: element bound
+        ref64, derr = down_combine_ref(hq.cpu().numpy(), hs.cpu().numpy(), perm.cpu().numpy(), ids, tw,
+                                       d["q2"], d["s2"], d["k"], tokens)
+        rep_dc = bf16_compare(out_bits[tokens], ref64, derr)
+        assert rep_dc["n_bound_violations"] == 0, rep_dc
+        # end to end against the oracle's pass from the same input
+        ref_e2e = _oracle_pass_tokens(qx_ref, sx_ref, ids, tw, d, tokens)
+        rep = bf16_compare(out_bits[tokens], ref_e2e)
+        rep.update({"down_combine_frobenius": rep_dc["frobenius"], "down_combine_max_abs_over_rms":
+                    rep_dc["max_abs_over_rms"], "requant_codes_differ_from_oracle": rq["n_codes_differ"],
+                    "requant_codes": rq["n"]})
+        print(f"pass {p + 1}", rep, flush=True)
+        record(f"moe two-pass T=16384 pass {p + 1} (512 tokens)", rep)
+        assert rep["frobenius"] <= 4e-3, rep
+        # the next pass's input: the combine's fused quantisation of this output
+        if p + 1 < len(d["routes"]):
+            _, xq_f, xs_f = w8.moe_w8a8_grouped(xq, xs, ids_d, tw_d, dv["q13"], dv["s13"], dv["q2"], dv["s2"],
+                                                quantize_output=True)
+            xq, xs = w8.quantize_per_token(out)
+            torch.cuda.synchronize()
+            assert np.array_equal(xq_f.cpu().numpy(), xq.cpu().numpy())
+            assert np.array_equal(xs_f.cpu().numpy(), xs.cpu().numpy())
+            x_bits = out_bits
 
 
 def test_all_slots_dropped_gives_zeros(small):

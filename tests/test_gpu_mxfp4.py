@@ -11,7 +11,9 @@
 * The fused MXFP4 output quantisation equals mxfp4_quantize of the BF16
   output and the oracle's quantiser, bit for bit.
 * Full pass: normalised Frobenius <= 4e-3 against the oracle, on small and
-  ragged shapes, the pages' expert shapes and the two-pass stack (pass 2
+  ragged shapes, groups of 512 rows or more (the 256 x 256 tiles, with a
+  ragged N tail and half K stages), the pages' expert shapes and the two-pass
+  stacks of the Praxis shape and of the 16384-token workload (pass 2
   teacher-forced); edge shapes (one token and one expert, H = I = 128,
   H = 8192, I = 2048, a zero token row) and 1024 routing groups in the
   slot-position order.
@@ -320,6 +322,68 @@ def test_two_pass_praxis(praxis):
     rep2 = bf16_compare(bf16_bits(outs[1])[tokens], ref2)
     print("mx pass 2 (teacher-forced)", rep2, flush=True)
     record("mxfp4 two-pass Praxis shape T=4096 pass 2 teacher-forced (256 tokens)", rep2)
+    assert rep2["frobenius"] <= 4e-3, rep2
+
+
+# Groups of 512 rows or more on average run the 256 x 256 tiles (smaller
+# averages run 128 x 128 or 64 x 128 tiles): the shapes the 16384-token
+# workload reaches, plus a ragged N tail, half K stages and one n-tile.
+MX_LARGE_TILE_MIN_ROWS = 512
+MX_LARGE_GROUPS = [
+    dict(T=1100, H=2176, I=384, E=2, k=1, n_outlier=3),   # N tail 2176 = 8 x 256 + 128; K 8.5 and 1.5 stages
+    dict(T=1100, H=256, I=1280, E=1, k=1, n_outlier=2),   # 5 K stages in the down projection, one n-tile
+    dict(T=4096, H=2048, I=512, E=2, k=2, n_outlier=4),   # the workload's H and I; more tiles than CUs
+]
+
+
+@pytest.mark.parametrize("cfg", MX_LARGE_GROUPS)
+@pytest.mark.parametrize("order", [0, 1])
+def test_large_groups(cfg, order):
+    print(f"[mx large groups] {cfg} order={order}", flush=True)
+    groups = cfg["E"] * (cfg["k"] if order else 1)
+    assert cfg["T"] * cfg["k"] // groups >= MX_LARGE_TILE_MIN_ROWS
+    d = quantized_mx_moe(**cfg, seed=23)
+    hq, hs, perm, offsets = _check_fused(d, order, order, sample=2048)
+    _check_down(d, hq, hs, perm, offsets, order=order, n_tokens=min(512, d["T"]))
+    if order == 0:
+        _check_gate_up_bf16(d)
+        dv = _dev(d)
+        ids, w = d["routes"][0]
+        out = w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"],
+                                   dv["s2"])
+        torch.cuda.synchronize()
+        tokens = np.sort(np.random.default_rng(5).choice(d["T"], min(256, d["T"]), replace=False))
+        rep = bf16_compare(bf16_bits(out)[tokens], _oracle_tokens(d["x32"], ids, w, d, tokens))
+        record(f"mxfp4 full pass large groups T={d['T']} H={d['H']} I={d['I']} E={d['E']} k={d['k']}", rep)
+        assert rep["frobenius"] <= 4e-3, rep
+
+
+def test_two_pass_workload_sampled():
+    """The 16384-token MXFP4 two-pass workload (H 2048, I 512, 64 experts,
+    top-8: about 2048 rows per group, the 256 x 256 tiles), as the benchmark
+    runs it: the fused stages on sampled rows and tokens, then both passes end
+    to end on 256 sampled tokens, pass 2 from the GPU's pass-1 output."""
+    d = quantized_mx_moe(T=16384, H=2048, I=512, E=64, k=8, n_outlier=20, passes=2, seed=0)
+    dv = _dev(d)
+    hq, hs, perm, offsets = _check_fused(d, sample=2048)
+    _check_down(d, hq, hs, perm, offsets, n_tokens=256)
+    routes_dev = [(to_dev(i), to_dev(w)) for i, w in d["routes"]]
+    ws = w8.moe_mxfp4_workspace(d["T"], d["H"], d["I"], d["E"], d["k"])
+    outs = w8.moe_mxfp4_ffn(to_dev_bf16(d["x_bits"]), routes_dev, dv["q13"], dv["s13"], dv["q2"], dv["s2"],
+                            workspace=ws)
+    torch.cuda.synchronize()
+    tokens = np.sort(np.random.default_rng(6).choice(d["T"], 256, replace=False))
+    ids1, w1 = d["routes"][0]
+    rep1 = bf16_compare(bf16_bits(outs[0])[tokens], _oracle_tokens(d["x32"], ids1, w1, d, tokens))
+    print("mx workload pass 1", rep1, flush=True)
+    record("mxfp4 two-pass T=16384 pass 1 (256 tokens)", rep1)
+    assert rep1["frobenius"] <= 4e-3, rep1
+    x2 = oracle.bf16_bits_to_f64(bf16_bits(outs[0])[tokens]).astype(np.float32)
+    ids2, w2 = d["routes"][1]
+    ref2, _, _ = oracle.moe_mxfp4_pass(x2, ids2[tokens], w2[tokens], d["q13"], d["s13"], d["q2"], d["s2"])
+    rep2 = bf16_compare(bf16_bits(outs[1])[tokens], ref2)
+    print("mx workload pass 2 (teacher-forced)", rep2, flush=True)
+    record("mxfp4 two-pass T=16384 pass 2 teacher-forced (256 tokens)", rep2)
     assert rep2["frobenius"] <= 4e-3, rep2
 
 

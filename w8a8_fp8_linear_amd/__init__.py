@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = [
-    "W8A8Error", "lib", "lib_path", "abi_version",
+    "W8A8Error", "lib", "lib_path", "abi_version", "e4m3_from_f32", "bf16_from_f32",
     "quantize_per_token", "w8a8_gemm", "w8a8_linear", "quantize_weight",
     "moe_route", "moe_gate_up_bf16", "moe_gate_up_swiglu_quant", "moe_down_combine",
     "w8a8_grouped_gemm", "moe_w8a8_grouped", "moe_workspace", "moe_ffn",
@@ -45,8 +45,10 @@ _SIGNATURES = {
                                  _c_ptr, ctypes.c_size_t, _c_ptr]),
     "moe_gate_up_bf16": (ctypes.c_int, [_c_ptr] * 7 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
     "moe_gate_up_swiglu_quant_workspace_bytes": (ctypes.c_size_t, [_c_i64] * 3),
-    "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 9 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr, ctypes.c_size_t,
-                                                                          _c_ptr]),
+    "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr, ctypes.c_size_t,
+                                                                           _c_ptr]),
+    "e4m3_from_f32": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "bf16_from_f32": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "moe_down_combine": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
     "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "w8a8_grouped_gemm": (ctypes.c_int, [_c_ptr] * 8 + [_c_i64] * 5 + [_c_ptr, ctypes.c_size_t, _c_ptr]),
@@ -244,6 +246,30 @@ def fp8_linear_single_launch(x, w_q, w_scale, out=None):
     return out
 
 
+def e4m3_from_f32(v):
+    """E4M3 codes (uint8, same shape) of float32 values clamped to +-448: the
+    encoding step every quantiser here ends with, run on the device."""
+    import torch
+
+    if not isinstance(v, torch.Tensor) or v.dtype != torch.float32 or not v.is_cuda or not v.is_contiguous():
+        raise TypeError("v must be a contiguous float32 tensor on a GPU")
+    q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check("e4m3_from_f32", lib().e4m3_from_f32(v.data_ptr(), v.numel(), q.data_ptr(), _stream(v)))
+    return q
+
+
+def bf16_from_f32(v):
+    """BF16 (round to nearest even) of float32 values: the rounding every BF16
+    result here ends with, run on the device."""
+    import torch
+
+    if not isinstance(v, torch.Tensor) or v.dtype != torch.float32 or not v.is_cuda or not v.is_contiguous():
+        raise TypeError("v must be a contiguous float32 tensor on a GPU")
+    y = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    _check("bf16_from_f32", lib().bf16_from_f32(v.data_ptr(), v.numel(), y.data_ptr(), _stream(v)))
+    return y
+
+
 def quantize_weight(w):
     """BF16 weight [out, in] -> (E4M3 [out, in], float32 [out]); the same per-row map."""
     return quantize_per_token(w)
@@ -325,12 +351,13 @@ def moe_gate_up_bf16(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int, o
 
 
 def moe_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk: int, order: int = 0,
-                             dst_row=None, workspace=None):
+                             dst_row=None, workspace=None, return_h=False):
     """Requantised h = silu(g) * u: (h_q uint8 [T*k, I], h_scale f32 [T*k]).
 
     The tiles follow perm/offsets (made with ``order``); a slot's h lands on
     its sorted row, or on ``dst_row[slot]`` when given (the slot_row of a
-    moe_route in the other order)."""
+    moe_route in the other order). With ``return_h`` also the float32 h rows
+    the codes were made from: (h_q, h_scale, h)."""
     import torch
 
     T, H = x_q.shape
@@ -346,20 +373,22 @@ def moe_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, w13_q, w13_scale, topk
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
     h_q = torch.empty((T * topk, I), dtype=torch.uint8, device=x_q.device)
     h_s = torch.empty((T * topk,), dtype=torch.float32, device=x_q.device)
+    h = torch.empty((T * topk, I), dtype=torch.float32, device=x_q.device) if return_h else None
     _check("moe_gate_up_swiglu_quant", lib().moe_gate_up_swiglu_quant(
         x_q.data_ptr(), x_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(),
         dst_row.data_ptr() if dst_row is not None else None, w13_q.data_ptr(), w13_scale.data_ptr(),
-        h_q.data_ptr(), h_s.data_ptr(), T, H, I, E, topk, order, workspace.data_ptr(), workspace.numel(),
-        _stream(x_q)))
-    return h_q, h_s
+        h_q.data_ptr(), h_s.data_ptr(), h.data_ptr() if return_h else None, T, H, I, E, topk, order,
+        workspace.data_ptr(), workspace.numel(), _stream(x_q)))
+    return (h_q, h_s, h) if return_h else (h_q, h_s)
 
 
 def moe_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, order: int = 0, out=None,
                      y=None):
     """Down projection of the sorted rows and the router-weighted combine: BF16 [T, H].
 
-    perm/offsets come from ``moe_route(..., order=order)``; ``y`` is BF16
-    scratch [T*k, H] for the per-slot products."""
+    perm/offsets come from ``moe_route(..., order=order)``; ``y`` is float32
+    scratch [T*k, H] for the per-slot weighted products, which the combine
+    sums in float32 and rounds to BF16 once."""
     import torch
 
     T, k = topk_w.shape
@@ -371,9 +400,9 @@ def moe_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_sca
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
     if y is None:
-        y = torch.empty((T * k, H), dtype=torch.bfloat16, device=h_q.device)
-    if y.numel() < T * k * H or y.dtype != torch.bfloat16:
-        raise ValueError("y must be bfloat16 with at least T * k * H elements")
+        y = torch.empty((T * k, H), dtype=torch.float32, device=h_q.device)
+    if y.numel() < T * k * H or y.dtype != torch.float32 or not y.is_contiguous():
+        raise ValueError("y must be contiguous float32 with at least T * k * H elements")
     _check("moe_down_combine", lib().moe_down_combine(
         h_q.data_ptr(), h_scale.data_ptr(), perm.data_ptr(), offsets.data_ptr(), topk_ids.data_ptr(),
         topk_w.data_ptr(), w2_q.data_ptr(), w2_scale.data_ptr(), out.data_ptr(), y.data_ptr(), T, H, I, E, k,
@@ -560,9 +589,9 @@ def moe_mxfp4_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, 
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h_q.device)
     if y is None:
-        y = torch.empty((T * k, H), dtype=torch.bfloat16, device=h_q.device)
-    if y.numel() < T * k * H or y.dtype != torch.bfloat16:
-        raise ValueError("y must be bfloat16 with at least T * k * H elements")
+        y = torch.empty((T * k, H), dtype=torch.float32, device=h_q.device)
+    if y.numel() < T * k * H or y.dtype != torch.float32 or not y.is_contiguous():
+        raise ValueError("y must be contiguous float32 with at least T * k * H elements")
     oq = os_ = None
     if quantize_output:
         oq = torch.empty((T, H // 2), dtype=torch.uint8, device=h_q.device)

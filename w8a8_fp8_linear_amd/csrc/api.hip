@@ -123,6 +123,28 @@ int w8a16_gemm(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale,
   return launch_status(w8a8::launch_w8a16_gemm(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
 }
 
+int e4m3_from_f32(const float* v, int64_t n, uint8_t* q_e4m3, hipStream_t stream) {
+  if (n < 0) return W8A8_ERR_BAD_SHAPE;
+  if (n > (int64_t(1) << 40)) return W8A8_ERR_UNSUPPORTED;
+  if (n == 0) return W8A8_OK;
+  if (!v || !q_e4m3) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(v) || !aligned16(q_e4m3)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_convert_e4m3(v, n, q_e4m3, stream));
+}
+
+int bf16_from_f32(const float* v, int64_t n, uint16_t* y_bf16, hipStream_t stream) {
+  if (n < 0) return W8A8_ERR_BAD_SHAPE;
+  if (n > (int64_t(1) << 40)) return W8A8_ERR_UNSUPPORTED;
+  if (n == 0) return W8A8_OK;
+  if (!v || !y_bf16) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(v) || !aligned16(y_bf16)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_convert_bf16(v, n, y_bf16, stream));
+}
+
 size_t fp8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0 || !mul_ok(M, K)) return 0;
   return (size_t)(align256(M * K) + align256(M * 4));
@@ -255,40 +277,40 @@ size_t moe_gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t to
 
 int moe_gate_up_swiglu_quant(const uint8_t* x_q, const float* x_scale, const int32_t* perm, const int32_t* offsets,
                              const int32_t* dst_row, const uint8_t* w13_q, const float* w13_scale, uint8_t* h_q,
-                             float* h_scale, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, int order,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             float* h_scale, float* h_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                             int order, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
   if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (I % kFusedIMultiple != 0) return W8A8_ERR_UNSUPPORTED;
   if (T == 0) return W8A8_OK;
   if (any_null({x_q, x_scale, perm, offsets, w13_q, w13_scale, h_q, h_scale, workspace})) return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale, h_q, h_scale, workspace}))
+  if (!all_aligned({x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale, h_q, h_scale, h_f32, workspace}))
     return W8A8_ERR_MISALIGNED;
   if (workspace_bytes < w8a8::gate_up_swiglu_quant_workspace_bytes(T, I, topk)) return W8A8_ERR_WORKSPACE;
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_gate_up_swiglu_quant(x_q, x_scale, perm, offsets, dst_row, w13_q, w13_scale, h_q,
-                                                         h_scale, T, H, I, E, topk, order, workspace, stream));
+                                                         h_scale, h_f32, T, H, I, E, topk, order, workspace, stream));
 }
 
 int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* perm, const int32_t* offsets,
                      const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const float* w2_scale,
-                     uint16_t* out_bf16, uint16_t* y_bf16, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                     uint16_t* out_bf16, float* y_f32, int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                      int order, hipStream_t stream) {
   const int c = check_moe_shape(T, H, I, E, topk);
   if (c != W8A8_OK) return c;
   if ((order != 0 && order != 1) || w8a8::route_groups(topk, E, order) > kMaxGroups) return W8A8_ERR_UNSUPPORTED;
   if (!mul_ok(T * topk, H) || !mul_ok(T * topk * H, 4)) return W8A8_ERR_BAD_SHAPE;
   if (T == 0) return W8A8_OK;
-  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16}))
+  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
     return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16}))
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
     return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
-                                                 out_bf16, y_bf16, nullptr, nullptr, T, H, I, E, topk, order, stream));
+                                                 out_bf16, y_f32, nullptr, nullptr, T, H, I, E, topk, order, stream));
 }
 
 size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -405,20 +427,20 @@ int moe_mxfp4_gate_up_swiglu_quant(const uint8_t* x_q, const uint8_t* x_scale, c
 
 int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int32_t* perm, const int32_t* offsets,
                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w2_q, const uint8_t* w2_scale,
-                           uint16_t* out_bf16, uint16_t* y_bf16, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
+                           uint16_t* out_bf16, float* y_f32, uint8_t* out_q, uint8_t* out_scale, int64_t T, int64_t H,
                            int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
   const int c = check_mx_moe(T, H, I, E, topk, order);
   if (c != W8A8_OK) return c;
   if (T == 0) return W8A8_OK;
-  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16}))
+  if (any_null({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32}))
     return W8A8_ERR_NULL_ARG;
   if ((out_q == nullptr) != (out_scale == nullptr)) return W8A8_ERR_NULL_ARG;
-  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_bf16, out_q, out_scale}))
+  if (!all_aligned({h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale, out_bf16, y_f32, out_q, out_scale}))
     return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_mx_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
-                                                    out_bf16, y_bf16, out_q, out_scale, T, H, I, E, topk, order,
+                                                    out_bf16, y_f32, out_q, out_scale, T, H, I, E, topk, order,
                                                     stream));
 }
 

@@ -1,6 +1,6 @@
 // Device helpers shared by the grouped (routed-expert) kernels of both
 // expert formats: the tile lookup over the device-side group offsets and the
-// ordered per-token sum of the BF16 slot rows.
+// ordered per-token sum of the float32 slot rows.
 #pragma once
 
 #include "device.h"
@@ -47,17 +47,17 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
   return false;
 }
 
-// Sum of a token's valid BF16 slot rows at columns c0 .. c0 + 7, in the
+// Sum of a token's valid float32 slot rows at columns c0 .. c0 + 7, in the
 // order j = 0, 1, ... in float32 (deterministic). The k rows of a token are
 // contiguous in y; they are loaded (non-temporal: each byte is read once)
 // before any is added, and a dropped slot's row is read but not used.
-__device__ inline void sum_slots8(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids, int64_t t,
+__device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __restrict__ ids, int64_t t,
                                   int topk, int Eids, int H, int c0, float4& a, float4& b) {
   a = make_float4(0.f, 0.f, 0.f, 0.f);
   b = a;
   constexpr int kBatch = 8;
   for (int j0 = 0; j0 < topk; j0 += kBatch) {
-    v4i u[kBatch];
+    v4f u[kBatch], v[kBatch];
     bool ok[kBatch];
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
@@ -65,14 +65,15 @@ __device__ inline void sum_slots8(const uint16_t* __restrict__ y, const int32_t*
       const int64_t slot = t * topk + (j < topk ? j : 0);
       const int id = ids[slot];
       ok[jj] = j < topk && id >= 0 && id < Eids;
-      u[jj] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(y + slot * H + c0));
+      const v4f* row = reinterpret_cast<const v4f*>(y + slot * H + c0);
+      u[jj] = __builtin_nontemporal_load(row);
+      v[jj] = __builtin_nontemporal_load(row + 1);
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
       if (!ok[jj]) continue;
-      const uint32_t w0 = (uint32_t)u[jj].x, w1 = (uint32_t)u[jj].y, w2 = (uint32_t)u[jj].z, w3 = (uint32_t)u[jj].w;
-      a.x += bf16_lo(w0); a.y += bf16_hi(w0); a.z += bf16_lo(w1); a.w += bf16_hi(w1);
-      b.x += bf16_lo(w2); b.y += bf16_hi(w2); b.z += bf16_lo(w3); b.w += bf16_hi(w3);
+      a.x += u[jj][0]; a.y += u[jj][1]; a.z += u[jj][2]; a.w += u[jj][3];
+      b.x += v[jj][0]; b.y += v[jj][1]; b.z += v[jj][2]; b.w += v[jj][3];
     }
   }
 }

@@ -12,6 +12,11 @@ namespace w8a8 {
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scale,
                                 hipStream_t stream);
 
+// The final conversions of the quantisers and of every BF16 result, on
+// caller-given float32 values: E4M3 of clamp(v, -448, 448), and BF16 RNE.
+hipError_t launch_convert_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t stream);
+hipError_t launch_convert_bf16(const float* v, int64_t n, uint16_t* y, hipStream_t stream);
+
 // Dense scaled FP8 GEMM: y[m,n] = bf16(sa[m] * sw[n] * sum_k a[m,k] w[n,k]).
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                        uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -51,21 +56,23 @@ hipError_t launch_grouped_gate_up_bf16(const uint8_t* xq, const float* xs, const
                                        int64_t topk, int order, hipStream_t stream);
 
 // dst_row (may be NULL): slot -> output row of h_q / h_scale; NULL keeps
-// the sorted order of perm. ws: gate_up_swiglu_quant_workspace_bytes bytes,
+// the sorted order of perm. h_out (may be NULL): where the float32 h rows go
+// (in the same rows as h_q) instead of the workspace.
+// ws: gate_up_swiglu_quant_workspace_bytes bytes,
 // whose first T * topk words (the row maxima) it clears first unless
 // amax_zeroed says an earlier launch on the stream already did.
 hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
-                                       const float* s13, uint8_t* qh, float* sh, int64_t T, int64_t H,
-                                       int64_t I, int64_t E, int64_t topk, int order, void* ws,
+                                       const float* s13, uint8_t* qh, float* sh, float* h_out, int64_t T,
+                                       int64_t H, int64_t I, int64_t E, int64_t topk, int order, void* ws,
                                        hipStream_t stream, bool amax_zeroed = false);
 
-// y: [T*topk, H] BF16 scratch (down_combine_scratch_bytes).
+// y: [T*topk, H] float32 scratch (down_combine_scratch_bytes).
 size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk);
 // out_q / out_s (both NULL or both set): also quantize_per_token(out).
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
                                const int32_t* offsets, const int32_t* ids, const float* tw,
-                               const uint8_t* w2, const float* s2, uint16_t* out, uint16_t* y,
+                               const uint8_t* w2, const float* s2, uint16_t* out, float* y,
                                uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I,
                                int64_t E, int64_t topk, int order, hipStream_t stream);
 
@@ -93,11 +100,11 @@ hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, 
                                           const uint8_t* s13, uint8_t* qh, uint8_t* sh, int64_t T, int64_t H,
                                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
-// y: [T*topk, H] BF16 scratch; out_q / out_s (both NULL or both set): also
+// y: [T*topk, H] float32 scratch; out_q / out_s (both NULL or both set): also
 // the MXFP4 quantisation of out.
 hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
-                                  uint16_t* out, uint16_t* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
+                                  uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
                                   int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
 size_t mx_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);

@@ -10,10 +10,8 @@
 // onto SGLang"). The expert activation, the gate/up layout, the requantised
 // expert input and the combine are not printed; the readings taken are:
 // W13[e] = [gate; up] rows, h = silu(g) * u in float32, one E4M3 scale per
-// routed copy (slot) of h, each routed copy's weighted output rounded to
-// BF16 (the model's dtype between the expert stage and the top-k sum, as in
-// the fused-MoE kernels the model is built on: sglang-metis 0.1.0, the
-// package description), out[t] = bf16(sum_j y[t,j]) with float32 sums.
+// routed copy (slot) of h, and out[t] = bf16(sum_j w[t,j] * y[t,j]) with the
+// weighted copies kept in float32 and summed in float32, rounded once.
 //
 // Kernels
 //  * route_count / route_scatter: slots t*k+j are grouped by expert (or by
@@ -36,16 +34,15 @@
 //      DOWN_Y     A = the requantised rows (sorted, contiguous), B = W2 of
 //                 the tile's expert; the epilogue applies the row scale, the
 //                 channel scale and the router weight and stores the slot's
-//                 BF16 product y to its own row.
+//                 float32 product y to its own row.
 //  * requant_rows: elementwise E4M3 requantisation of h once the row maxima
 //    are known (scale = amax / 448, correctly rounded division, RNE).
-//  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots (BF16
-//    rows, float32 sums), added
-//    in the fixed order j = 0, 1, ... (deterministic, no atomics; float32
-//    atomics measured ~3x slower than this whole stage). The k rows of a
-//    token are contiguous, so this is one streaming pass. combine_quant also
-//    quantises each output row per token (the next pass's input) in the
-//    same pass.
+//  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots
+//    (float32 rows and sums, one rounding), added in the fixed order
+//    j = 0, 1, ... (deterministic, no atomics; float32 atomics measured ~3x
+//    slower than this whole stage). The k rows of a token are contiguous, so
+//    this is one streaming pass. combine_quant also quantises each output row
+//    per token (the next pass's input) in the same pass.
 #include <algorithm>
 
 #include "device.h"
@@ -220,8 +217,8 @@ struct Grouped {
   static constexpr int kStage = kRows * 128;
   static constexpr int kRowsPerPass = kThreads / 8;    // rows one load instruction covers
   static constexpr int kLoadsB = BN / kRowsPerPass, kLoadsA = BM / kRowsPerPass;
-  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP, DOWN_Y)
-  static constexpr int kEpi = (MODE == kGateUp || MODE == kDownY) ? BM * kEpiStride : 0;
+  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP)
+  static constexpr int kEpi = MODE == kGateUp ? BM * kEpiStride : 0;
   static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
   static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
   static_assert(kRowsPerPass % 8 == 0, "the loader's chunk swizzle needs 8-row passes");
@@ -239,8 +236,8 @@ struct GroupedArgs {
   const uint8_t* B;         // [E, N, K] weight codes
   const float* sB;          // [E, N] weight row scales
   const float* tw;          // DOWN_Y: router weights [slots]
-  uint16_t* out_bf16;       // GATE_UP: [rows, N]; DOWN_Y: y [slots, N]
-  float* out_f32;           // GATE_UP_H: h [rows, N / 2]
+  uint16_t* out_bf16;       // GATE_UP: [rows, N]
+  float* out_f32;           // GATE_UP_H: h [rows, N / 2]; DOWN_Y: y [slots, N]
   uint32_t* row_amax;       // GATE_UP_H: max |h| bits per output row (cleared by the caller)
   const int32_t* dst_row;   // GATE_UP_H: slot -> output row (NULL: the sorted row itself)
   int N, K, tiles_n, tiles_m_max;
@@ -261,10 +258,10 @@ struct GroupedArgs {
 //             partial max |h| with an integer atomicMax on the float bits
 //             (order-independent, so the row maximum is exact).
 //  DOWN_Y:    A row = h codes of sorted row r (contiguous); the epilogue
-//             stages bf16(w[slot] * sA[r] * sB[e, n] * acc) in LDS and
-//             stores each tile row as 16-byte chunks of one contiguous row
-//             segment of row `slot` of out_bf16 [T * topk, N] (every slot is
-//             written once).
+//             stores w[slot] * sA[r] * sB[e, n] * acc in float32 to row
+//             `slot` of out_f32 [T * topk, N] (every slot is written once),
+//             straight from registers: a lane holds 4 consecutive columns of
+//             one row, one 16-byte store.
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
@@ -395,39 +392,25 @@ void grouped_tiled(const GroupedArgs p) {
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
   if (MODE == kDownY) {
-    // Scale and round to BF16, stage in LDS, then store whole row segments:
-    // measured 12% faster for this stage than 8-byte stores straight from
-    // registers (each of those writes 32 bytes of 16 scattered rows).
-    float4 sWv[C::SN];  // the weight scales, loaded together before the barrier
+    // The weighted copy in float32. Each lane's 4 values are consecutive
+    // columns of one row, so the stores go out straight from registers as
+    // 16-byte row pieces (measured faster than staging float32 rows in LDS,
+    // which would also need twice the BF16 staging space).
 #pragma unroll
     for (int i = 0; i < C::SN; ++i) {
-      const int nl = wn * C::WN + i * 16 + 4 * g;
-      sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::SN; ++i) {
-      const int nl = wn * C::WN + i * 16 + 4 * g;
-      const float4 sW = sWv[i];
+      const int n = n0 + wn * C::WN + i * 16 + 4 * g;
+      const float4 sW = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) {
         const int ml = wm * C::WM + j * 16 + r16;
+        const int slot = row_tok[ml];
         const float s = row_scale[ml];
         const v4f a = acc[i][j];
-        *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) =
-            make_uint2(bf16x2_rne(a[0] * s * sW.x, a[1] * s * sW.y),
-                       bf16x2_rne(a[2] * s * sW.z, a[3] * s * sW.w));
+        if (slot >= 0 && n < N)
+          store16_nt(p.out_f32 + (int64_t)slot * N + n,
+                     make_float4(a[0] * s * sW.x, a[1] * s * sW.y, a[2] * s * sW.z, a[3] * s * sW.w));
       }
-    }
-    __syncthreads();
-    constexpr int kRowChunks = BN / 8;
-    for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
-      const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
-      const int slot = row_tok[row];
-      if (slot >= 0 && n0 + col < N)
-        store16_nt(p.out_bf16 + (int64_t)slot * N + n0 + col,
-                   *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
     }
     return;
   }
@@ -564,7 +547,7 @@ __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, i
 
 // out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots.
 // One thread per 8 columns.
-__global__ __launch_bounds__(256) void combine_slots(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y, const int32_t* __restrict__ ids,
                                                      int64_t T, int topk, int Eids, int H,
                                                      uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -583,7 +566,7 @@ __global__ __launch_bounds__(256) void combine_slots(const uint16_t* __restrict_
 // makes of out[t]: amax on the BF16 bits, s = fl32(amax / 448), codes of
 // fl32(x / s) (the same shared quantiser code).
 template <int PER>
-__global__ __launch_bounds__(256) void combine_quant(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y, const int32_t* __restrict__ ids,
                                                      int topk, int Eids, int H, uint16_t* __restrict__ out,
                                                      uint8_t* __restrict__ q, float* __restrict__ qs) {
   __shared__ uint32_t wmax[4];
@@ -722,14 +705,14 @@ size_t gate_up_swiglu_quant_workspace_bytes(int64_t T, int64_t I, int64_t topk) 
 // Workspace: row maxima [T*k] (uint32 float bits) | h [T*k, I] float32.
 hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const int32_t* perm,
                                        const int32_t* offsets, const int32_t* dst_row, const uint8_t* w13,
-                                       const float* s13, uint8_t* qh, float* sh, int64_t T, int64_t H, int64_t I,
-                                       int64_t E, int64_t topk, int order, void* ws, hipStream_t stream,
-                                       bool amax_zeroed) {
+                                       const float* s13, uint8_t* qh, float* sh, float* h_out, int64_t T,
+                                       int64_t H, int64_t I, int64_t E, int64_t topk, int order, void* ws,
+                                       hipStream_t stream, bool amax_zeroed) {
   const int64_t n = T * topk;
   if (n == 0) return hipSuccess;
   const int G = (int)route_groups(topk, E, order);
   uint32_t* amax = static_cast<uint32_t*>(ws);
-  float* h = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * 4));
+  float* h = h_out ? h_out : reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * 4));
   if (!amax_zeroed) hipLaunchKernelGGL(fill_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, amax, n);
   GroupedArgs a = gate_up_args(xq, xs, perm, offsets, G, w13, s13, T, H, I, E, topk);
   a.out_f32 = h;
@@ -747,7 +730,7 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
 // to its own row of y), then the per-token combine.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm, const int32_t* offsets,
                                const int32_t* ids, const float* tw, const uint8_t* w2, const float* s2, uint16_t* out,
-                               uint16_t* y, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I, int64_t E,
+                               float* y, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I, int64_t E,
                                int64_t topk, int order, hipStream_t stream) {
   GroupedArgs a{};
   a.A = qh;
@@ -761,7 +744,7 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   a.B = w2;
   a.sB = s2;
   a.tw = tw;
-  a.out_bf16 = y;
+  a.out_f32 = y;
   a.N = (int)H;
   a.K = (int)I;
   const hipError_t err = run_grouped_auto<kDownY>(a, T * topk, T * topk / a.G, stream);
@@ -785,12 +768,12 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   return launch_quantize_rows(out, T, H, out_q, out_s, stream);
 }
 
-size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk) { return (size_t)(T * topk * H * 2); }
+size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk) { return (size_t)(T * topk * H * 4); }
 
 // Workspace of the full pass:
 //   counts | offsets | perm | route scratch | qh | sh | amax | big
 // where big holds h [T*k, I] float32 during the gate/up and then the
-// weighted slot products y [T*k, H] BF16 of the down projection.
+// weighted slot products y [T*k, H] float32 of the down projection.
 struct MoeLayout {
   int64_t counts, offsets, perm, route, qh, sh, amax, big, total;
 };
@@ -806,7 +789,7 @@ static MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t 
   L.qh = o; o += align256(n * I);
   L.sh = o; o += align256(n * 4);
   L.amax = o; o += align256(n * 4);  // amax | big is the gate/up stage's workspace
-  L.big = o; o += std::max(align256(n * I * 4), align256(n * H * 2));
+  L.big = o; o += std::max(align256(n * I * 4), align256(n * H * 4));
   L.total = o;
   return L;
 }
@@ -832,10 +815,10 @@ hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, co
   hipError_t err = launch_route(ids, T, topk, E, 0, counts, offsets, perm, nullptr, b + L.route, stream,
                                 reinterpret_cast<uint32_t*>(b + L.amax), T * topk);
   if (err != hipSuccess) return err;
-  err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, T, H, I, E, topk, 0,
+  err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, nullptr, T, H, I, E, topk, 0,
                                     b + L.amax, stream, true);
   if (err != hipSuccess) return err;
-  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<uint16_t*>(b + L.big), out_q,
+  return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<float*>(b + L.big), out_q,
                              out_s, T, H, I, E, topk, 0, stream);
 }
 

@@ -35,11 +35,11 @@
 //                 block), the exponent and the E2M1 codes are made in
 //                 registers and stored: no float32 h round trip, no row
 //                 maximum, no atomics, no second kernel;
-//      DOWN_Y     per-slot BF16 y = bf16(w[slot] * acc), staged in LDS and
-//                 stored as whole row segments of the slot's own row.
-//  * combine_mx: the ordered per-token slot sum of the FP8 combine, with the
-//    BF16 result optionally quantised to MXFP4 in the same pass (the next
-//    pass's expert input).
+//      DOWN_Y     per-slot float32 y = w[slot] * acc, stored straight from
+//                 registers to the slot's own row.
+//  * combine_mx: the ordered per-token slot sum of the FP8 combine (float32
+//    rows and sums, one BF16 rounding), with the BF16 result optionally
+//    quantised to MXFP4 in the same pass (the next pass's expert input).
 #include "device.h"
 #include "grouped.h"
 #include "launch.h"
@@ -145,8 +145,8 @@ struct MxTile {
   static constexpr int kLoadsB = BN / kRowsPerPass, kLoadsA = BM / kRowsPerPass;
   static constexpr int kScaleDw = kRows * 2;           // scale dwords per stage
   static constexpr int kScaleLoads = (kScaleDw + kThreads - 1) / kThreads;
-  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP, DOWN_Y)
-  static constexpr int kEpi = (MODE == kMxGateUp || MODE == kMxDownY) ? BM * kEpiStride : 0;
+  static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP)
+  static constexpr int kEpi = MODE == kMxGateUp ? BM * kEpiStride : 0;
   static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
   static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
   static_assert(kRowsPerPass % 8 == 0, "the loader's chunk swizzle needs 8-row passes");
@@ -166,7 +166,8 @@ struct MxArgs {
   const uint8_t* B;         // [E, N, K/2] weight codes
   const uint8_t* sB;        // [E, N, K/32] weight scales
   const float* tw;          // DOWN_Y: router weights [slots]
-  uint16_t* out_bf16;       // GATE_UP: [rows, N]; DOWN_Y: y [slots, N]
+  uint16_t* out_bf16;       // GATE_UP: [rows, N]
+  float* out_f32;           // DOWN_Y: y [slots, N]
   uint8_t* out_q;           // GATE_UP_Q: h codes [rows, N/4]
   uint8_t* out_s;           // GATE_UP_Q: h scales [rows, N/64]
   const int32_t* dst_row;   // GATE_UP_Q: slot -> output row (NULL: the sorted row)
@@ -346,28 +347,20 @@ void mx_grouped(const MxArgs p) {
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
   if (MODE == kMxDownY) {
-    __syncthreads();
+    // y = w * acc in float32, straight from registers: each lane's 4 values
+    // are consecutive columns of one row, one 16-byte store.
 #pragma unroll
     for (int i = 0; i < C::SN; ++i) {
-      const int nl = wn * C::WN + i * 16 + 4 * g;
+      const int n = n0 + wn * C::WN + i * 16 + 4 * g;
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) {
         const int ml = wm * C::WM + j * 16 + r16;
+        const int slot = row_tok[ml];
         const float w = row_w[ml];
         const v4f a = acc[i][j];
-        *reinterpret_cast<uint2*>(smem + ml * C::kEpiStride + nl * 2) =
-            make_uint2(bf16x2_rne(a[0] * w, a[1] * w),
-                       bf16x2_rne(a[2] * w, a[3] * w));
+        if (slot >= 0 && n < N)
+          store16_nt(p.out_f32 + (int64_t)slot * N + n, make_float4(a[0] * w, a[1] * w, a[2] * w, a[3] * w));
       }
-    }
-    __syncthreads();
-    constexpr int kRowChunks = BN / 8;
-    for (int c = tid; c < BM * kRowChunks; c += C::kThreads) {
-      const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
-      const int slot = row_tok[row];
-      if (slot >= 0 && n0 + col < N)
-        store16_nt(p.out_bf16 + (int64_t)slot * N + n0 + col,
-                   *reinterpret_cast<const uint4*>(smem + row * C::kEpiStride + col * 2));
     }
     return;
   }
@@ -443,7 +436,7 @@ void mx_grouped(const MxArgs p) {
 // the BF16 row (exactly what mx_quant_bf16 makes of it). One thread per 8
 // columns; H % 32 == 0, so a block's four threads form an aligned quad.
 template <bool QUANT>
-__global__ __launch_bounds__(256) void combine_mx(const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, const int32_t* __restrict__ ids,
                                                   int64_t T, int topk, int Eids, int H, uint16_t* __restrict__ out,
                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -534,7 +527,7 @@ hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, 
 
 hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
-                                  uint16_t* out, uint16_t* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
+                                  uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
                                   int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
   MxArgs a{};
   a.A = qh;
@@ -548,7 +541,7 @@ hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const in
   a.B = w2;
   a.sB = s2;
   a.tw = tw;
-  a.out_bf16 = y;
+  a.out_f32 = y;
   a.N = (int)H;
   a.K = (int)I;
   const hipError_t err = run_mx_auto<kMxDownY>(a, T * topk, T * topk / a.G, stream);
@@ -565,7 +558,7 @@ hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const in
 }
 
 // Workspace of the full pass: counts | offsets | perm | route scratch |
-// h codes [T*k, I/2] | h scales [T*k, I/32] | y [T*k, H] BF16.
+// h codes [T*k, I/2] | h scales [T*k, I/32] | y [T*k, H] float32.
 struct MxLayout {
   int64_t counts, offsets, perm, route, qh, sh, y, total;
 };
@@ -581,7 +574,7 @@ static MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t to
   L.route = o; o += (int64_t)route_workspace_bytes(T, topk, E);
   L.qh = o; o += al(n * I / 2);
   L.sh = o; o += al(n * I / 32);
-  L.y = o; o += al(n * H * 2);
+  L.y = o; o += al(n * H * 4);
   L.total = o;
   return L;
 }
@@ -605,7 +598,7 @@ hipError_t launch_mx_moe(const uint8_t* xq, const uint8_t* xs, const int32_t* id
                                        0, stream);
   if (err != hipSuccess) return err;
   return launch_mx_down_combine(b + L.qh, b + L.sh, perm, offsets, ids, tw, w2, s2, out,
-                                reinterpret_cast<uint16_t*>(b + L.y), out_q, out_s, T, H, I, E, topk, 0, stream);
+                                reinterpret_cast<float*>(b + L.y), out_q, out_s, T, H, I, E, topk, 0, stream);
 }
 
 }  // namespace w8a8

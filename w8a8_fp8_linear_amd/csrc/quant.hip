@@ -85,7 +85,53 @@ __global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restr
   if (lane == 0) scale[row] = s;
 }
 
+// The two conversions every output of this library ends with, applied to
+// caller-given float32 values: the E4M3 encoding of the quantisers (clamp
+// to +-448, then the hardware round-to-nearest-even conversion, e4m3x4) and
+// the BF16 rounding of every BF16 result (bf16x2_rne). Four values per
+// thread; the tail is guarded per element.
+__global__ __launch_bounds__(256) void convert_e4m3(const float* __restrict__ v, int64_t n, uint8_t* __restrict__ q) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = i + k < n ? clamp448(v[i + k]) : 0.f;
+  const uint32_t w = e4m3x4(a[0], a[1], a[2], a[3]);
+  if (i + 4 <= n) {
+    *reinterpret_cast<uint32_t*>(q + i) = w;
+  } else {
+    for (int k = 0; i + k < n; ++k) q[i + k] = (uint8_t)(w >> (8 * k));
+  }
+}
+
+__global__ __launch_bounds__(256) void convert_bf16(const float* __restrict__ v, int64_t n, uint16_t* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = i + k < n ? v[i + k] : 0.f;
+  const uint32_t lo = bf16x2_rne(a[0], a[1]), hi = bf16x2_rne(a[2], a[3]);
+  if (i + 4 <= n) {
+    *reinterpret_cast<uint2*>(y + i) = make_uint2(lo, hi);
+  } else {
+    const uint32_t w[2] = {lo, hi};
+    for (int k = 0; i + k < n; ++k) y[i + k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_convert_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_e4m3, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream, v, n, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_bf16(const float* v, int64_t n, uint16_t* y, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_bf16, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream, v, n, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scale,
                                 hipStream_t stream) {
