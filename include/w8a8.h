@@ -59,7 +59,8 @@ enum {
   W8A8_ERR_UNSUPPORTED = 4,   /* a size the kernels do not handle (see each call)  */
   W8A8_ERR_WORKSPACE = 5,     /* workspace smaller than the *_workspace_bytes size */
   W8A8_ERR_DEVICE = 6,        /* the current device is not gfx950, or no device    */
-  W8A8_ERR_LAUNCH = 7         /* the HIP runtime refused a launch                  */
+  W8A8_ERR_LAUNCH = 7,        /* the HIP runtime refused a launch                  */
+  W8A8_ERR_SCRATCH = 8        /* the sizes need more than the static scratch holds */
 };
 
 /* W8A8_ABI_VERSION of the built library. */
@@ -177,6 +178,26 @@ size_t fp8_linear_workspace_bytes(int64_t M, int64_t K);
  */
 int fp8_linear(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
                int64_t N, int64_t K, int fast_math, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fp8_linear_noalloc — fp8_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, dispatch and results as fp8_linear (bit
+ * for bit), without the workspace: the quantised input (M*K codes + M scales,
+ * each rounded up to 256 bytes) goes to a static device array of the library,
+ * fp8_linear_noalloc_max_bytes() bytes (64 MiB) per GPU, held until the
+ * process ends. The call allocates nothing (no hipMalloc, no allocating
+ * library routine); on its first call on a device it looks up that device's
+ * address of the array.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * The array needs no clearing: each call writes every byte it reads.
+ * Errors: as fp8_linear (no WORKSPACE), plus SCRATCH when the FP8 path would
+ * need more than fp8_linear_noalloc_max_bytes() (checked before any launch).
+ */
+size_t fp8_linear_noalloc_max_bytes(void);
+int fp8_linear_noalloc(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
+                       int64_t N, int64_t K, int fast_math, hipStream_t stream);
 
 /*
  * fp8_linear_single_launch — the FP8 multiply of fp8_linear (per-token

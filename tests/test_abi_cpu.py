@@ -13,7 +13,7 @@ import w8a8_fp8_linear_amd as w8
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DECL = re.compile(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
 
-OK, NULL, SHAPE, MIS, UNSUP, WS, DEV, LAUNCH = range(8)
+OK, NULL, SHAPE, MIS, UNSUP, WS, DEV, LAUNCH, SCRATCH = range(9)
 
 
 def _declared():
@@ -40,7 +40,7 @@ def test_binding_covers_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert w8.abi_version() == 2
-    for s in range(8):
+    for s in range(9):
         assert w8.lib().w8a8_status_string(s)
     assert w8.lib().w8a8_status_string(99) == b"unknown status"
 
@@ -177,3 +177,19 @@ def test_gate_up_swiglu_quant_h_output_alignment():
     assert f(*args, 8, 256, 128, 2, 2, 0, P, 1 << 30, None) == MIS
     args[9] = None                                  # h_f32 is optional
     assert f(*args, 8, 256, 128, 2, 2, 0, P, 1 << 30, None) == DEV
+
+
+def test_fp8_linear_noalloc_argument_errors():
+    f = w8.lib().fp8_linear_noalloc
+    limit = w8.lib().fp8_linear_noalloc_max_bytes()
+    assert limit == 64 << 20
+    assert f(P, P, P, P, -1, 16, 16, 1, None) == SHAPE
+    assert f(P, P, P, P, 64, 16, 24, 1, None) == UNSUP
+    # the FP8 path of 8192 x 8192 needs 64 MiB of codes plus the scales: refused before any launch
+    assert f(P, P, P, P, 8192, 16, 8192, 1, None) == SCRATCH
+    assert f(P, P, P, P, 8192, 16, 8192, 0, None) == DEV      # default maths: no scratch
+    assert f(P, P, P, P, 16, 16, 2048, 1, None) == DEV        # single launch: no scratch
+    assert f(P, P, P, P, 4096, 16, 2048, 1, None) == DEV      # fits
+    assert f(P, P, P, P, 0, 16, 16, 1, None) == OK
+    assert f(None, P, P, P, 64, 16, 16, 1, None) == NULL
+    assert f(P, P, P, P + 8, 64, 16, 16, 1, None) == MIS

@@ -40,6 +40,9 @@ _SIGNATURES = {
     "fp8_linear_single_launch": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
     "fp8_linear": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr,
                                   ctypes.c_size_t, _c_ptr]),
+    "fp8_linear_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "fp8_linear_noalloc": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                          _c_ptr]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                  _c_ptr, ctypes.c_size_t, _c_ptr]),
@@ -221,6 +224,31 @@ def fp8_linear(x, w_q, w_scale, fast_math=True, out=None, workspace=None):
     wlen = workspace.numel() if workspace is not None else 0
     _check("fp8_linear", lib().fp8_linear(x.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(), out.data_ptr(), M, N, K,
                                           1 if fast_math else 0, wptr, wlen, _stream(x)))
+    return out
+
+
+def fp8_linear_noalloc(x, w_q, w_scale, fast_math=True, out=None):
+    """fp8_linear with the quantised input in the library's static device
+    scratch instead of a workspace: the library allocates nothing. ``out`` is
+    allocated here when not given (pass it to allocate nothing at all). Calls
+    that overlap on one GPU share the scratch and race."""
+    import torch
+
+    _want(x, torch.bfloat16, 2, "x")
+    _want(w_q, torch.uint8, 2, "w_q")
+    _want(w_scale, torch.float32, 1, "w_scale")
+    M, K = x.shape
+    N, K2 = w_q.shape
+    if K2 != K or w_scale.shape[0] != N:
+        raise ValueError("shape mismatch between x, w_q and w_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _want(out, torch.bfloat16, 2, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check("fp8_linear_noalloc", lib().fp8_linear_noalloc(x.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(),
+                                                          out.data_ptr(), M, N, K, 1 if fast_math else 0,
+                                                          _stream(x)))
     return out
 
 

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/w8a8.h"
 #include "launch.h"
@@ -80,6 +81,7 @@ const char* w8a8_status_string(int status) {
     case W8A8_ERR_WORKSPACE: return "workspace too small";
     case W8A8_ERR_DEVICE: return "current device is not gfx950";
     case W8A8_ERR_LAUNCH: return "kernel launch failed";
+    case W8A8_ERR_SCRATCH: return "size exceeds the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -173,6 +175,76 @@ int fp8_linear(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale,
   if (M <= kFusedFasterMaxM && K <= w8a8::kFusedDecodeMaxK)
     return launch_status(w8a8::launch_quant_gemm_decode(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
   uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(xq + align256(M * K));
+  const hipError_t e = w8a8::launch_quantize_rows(x_bf16, M, K, xq, xs, stream);
+  if (e != hipSuccess) return launch_status(e);
+  return launch_status(w8a8::launch_gemm(xq, xs, w_q, w_scale, y_bf16, M, N, K, stream));
+}
+
+}  // extern "C"
+
+// ---- fp8_linear without allocation ------------------------------------------
+namespace {
+
+// The quantised input of fp8_linear_noalloc: codes [M, K], then the M row
+// scales, each block 256-byte aligned. One copy per GPU, held until the
+// process ends. The name is a host-side stand-in; kernels get the address
+// hipGetSymbolAddress reports for the current device.
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of `scratch`, looked up once per device (with that
+// device current). NULL if the lookup fails.
+uint8_t* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (dev < kMaxDevices) {
+    uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < kMaxDevices) {
+    uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (dev < kMaxDevices) g_scratch_ptr[dev].store(static_cast<uint8_t*>(ptr), std::memory_order_release);
+  return static_cast<uint8_t*>(ptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8_linear_noalloc_max_bytes(void) { return (size_t)kNoAllocScratchBytes; }
+
+int fp8_linear_noalloc(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,
+                       int64_t N, int64_t K, int fast_math, hipStream_t stream) {
+  const int c = check_dense_shape(M, N, K);
+  if (c != W8A8_OK) return c;
+  const bool fp8_path = fast_math != 0 && M > kFastMathMinTokens;
+  const bool needs_scratch = fp8_path && !(M <= kFusedFasterMaxM && K <= w8a8::kFusedDecodeMaxK);
+  if (needs_scratch && fp8_linear_workspace_bytes(M, K) > (size_t)kNoAllocScratchBytes) return W8A8_ERR_SCRATCH;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!x_bf16 || !w_q || !w_scale || !y_bf16) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y_bf16)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  if (!fp8_path) return launch_status(w8a8::launch_w8a16_gemm(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
+  if (!needs_scratch)
+    return launch_status(w8a8::launch_quant_gemm_decode(x_bf16, w_q, w_scale, y_bf16, M, N, K, stream));
+  uint8_t* xq = device_scratch();
+  if (!xq) return W8A8_ERR_LAUNCH;
   float* xs = reinterpret_cast<float*>(xq + align256(M * K));
   const hipError_t e = w8a8::launch_quantize_rows(x_bf16, M, K, xq, xs, stream);
   if (e != hipSuccess) return launch_status(e);
