@@ -226,6 +226,27 @@ def bench_decode(Ms=(8, 1, 32), n_buffers=40, reps=5):
             "frac_hbm_peak": wbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "weight_bytes": wbytes,
         }
+    # The read floor: the same 40 rotated weight buffers, the same graph-replayed
+    # launch pattern, a kernel of the decode GEMM's launch shape that only reads
+    # the 16.8 MB (read_probe), and an empty launch of the same grid.
+    sink = torch.empty(int(w8.lib().read_probe_sink_words(N * K)) + 4, dtype=torch.int32, device="cuda")
+    probes = [lambda j=j: w8.read_probe(wqs[j], sink) for j in range(n_buffers)]
+    for fn in probes:
+        fn()
+    torch.cuda.synchronize()
+    rounds, method = _per_launch_ms(probes, reps, stream)
+    floor = sum(rounds) / len(rounds)
+    launches0 = [lambda: w8.read_probe(wqs[0][:1].view(-1)[:16], sink) for _ in range(n_buffers)]
+    r0, _ = _per_launch_ms(launches0, reps, stream)
+    out["read_floor"] = {
+        "what": "read_probe: every byte of each 16.8 MB weight buffer read in the decode GEMM's launch shape, "
+                "nothing else; same buffers and graph-replayed pattern",
+        "us_avg": 1e3 * floor, "GBs": N * K / (floor * 1e-3) / 1e9,
+        "frac_hbm_peak": N * K / (floor * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "launch_us_16_bytes": 1e3 * sum(r0) / len(r0), "timing": method,
+    }
+    for M in Ms:
+        out[f"M{M}"]["over_read_floor"] = out[f"M{M}"]["kernel_us_avg"] / (1e3 * floor)
     return out
 
 

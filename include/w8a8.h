@@ -136,6 +136,22 @@ int e4m3_from_f32(const float* v, int64_t n, uint8_t* q_e4m3, hipStream_t stream
 int bf16_from_f32(const float* v, int64_t n, uint16_t* y_bf16, hipStream_t stream);
 
 /*
+ * read_probe — the read floor of the decode weight stream, for measurement.
+ *
+ * A decode step is bound by how fast the GPU reads the weights (Lernex/
+ * Metis-1.6-Logos-FP8, "What --fast-math does"). This call reads every byte
+ * of p in the decode GEMM's launch shape (one 256-thread workgroup per
+ * 32 KB, each lane's 16-byte loads issued together) and does nothing else:
+ * sink[b] = XOR of the 32-bit words of block b. Timed like the decode GEMM,
+ * it is the floor that GEMM's weight stream is compared with.
+ *   p      [bytes] device data; bytes a multiple of 16, at most 2^40
+ *   sink   [read_probe_sink_words(bytes)] uint32 output
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, DEVICE, LAUNCH.
+ */
+int64_t read_probe_sink_words(int64_t bytes);
+int read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+/*
  * w8a16_gemm — the default maths: BF16 activations times the E4M3 weights
  * widened to BF16, on the BF16 matrix units.
  *

@@ -11,7 +11,7 @@ import pytest
 import w8a8_fp8_linear_amd as w8
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-DECL = re.compile(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
+DECL = re.compile(r"^\s*(?:const\s+)?(?:int64_t|int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
 
 OK, NULL, SHAPE, MIS, UNSUP, WS, DEV, LAUNCH, SCRATCH = range(9)
 
@@ -193,3 +193,16 @@ def test_fp8_linear_noalloc_argument_errors():
     assert f(P, P, P, P, 0, 16, 16, 1, None) == OK
     assert f(None, P, P, P, 64, 16, 16, 1, None) == NULL
     assert f(P, P, P, P + 8, 64, 16, 16, 1, None) == MIS
+
+
+def test_read_probe_argument_errors():
+    f = w8.lib().read_probe
+    assert w8.lib().read_probe_sink_words(16809984) == 513
+    assert w8.lib().read_probe_sink_words(32768) == 1
+    assert f(P, -16, P, None) == SHAPE
+    assert f(P, 24, P, None) == UNSUP
+    assert f(P, 0, P, None) == OK
+    assert f(None, 32, P, None) == NULL
+    assert f(P, 32, None, None) == NULL
+    assert f(P + 8, 32, P, None) == MIS
+    assert f(P, 32, P, None) == DEV

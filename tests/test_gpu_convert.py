@@ -97,3 +97,15 @@ def test_conversion_ragged_lengths():
         assert np.array_equal(w8.e4m3_from_f32(v).cpu().numpy(), oracle.encode_bits(np.clip(x, -448, 448)))
         got = w8.bf16_from_f32(v).view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, oracle.round_to_bf16_bits(x.astype(np.float64)))
+
+
+@pytest.mark.parametrize("nbytes", [16, 32768, 16809984, 100016])
+def test_read_probe_checksums(nbytes):
+    """read_probe reads every byte: its per-32 KB XOR words match the host's."""
+    rng = np.random.default_rng(nbytes)
+    data = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    sink = w8.read_probe(torch.from_numpy(data).cuda()).cpu().numpy().view(np.uint32)
+    padded = np.zeros(-(-nbytes // 32768) * 32768, np.uint8)
+    padded[:nbytes] = data
+    want = np.bitwise_xor.reduce(padded.view(np.uint32).reshape(-1, 8192), axis=1)
+    assert np.array_equal(sink[:want.size], want)

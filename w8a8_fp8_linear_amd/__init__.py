@@ -51,6 +51,8 @@ _SIGNATURES = {
     "moe_gate_up_swiglu_quant": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr, ctypes.c_size_t,
                                                                            _c_ptr]),
     "e4m3_from_f32": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "read_probe_sink_words": (ctypes.c_int64, [_c_i64]),
+    "read_probe": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "bf16_from_f32": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "moe_down_combine": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
     "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
@@ -296,6 +298,24 @@ def bf16_from_f32(v):
     y = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
     _check("bf16_from_f32", lib().bf16_from_f32(v.data_ptr(), v.numel(), y.data_ptr(), _stream(v)))
     return y
+
+
+def read_probe(t, sink=None):
+    """Read every byte of the contiguous device tensor t in the decode GEMM's
+    launch shape, doing nothing else (the weight stream's read floor). Returns
+    the sink: one uint32 XOR word per 32 KB block."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("t must be a contiguous tensor on a GPU")
+    nbytes = t.numel() * t.element_size()
+    words = int(lib().read_probe_sink_words(nbytes))
+    if sink is None:
+        sink = torch.empty(max(words, 4), dtype=torch.int32, device=t.device)
+    if sink.numel() < words or sink.dtype != torch.int32:
+        raise ValueError("sink must be int32 with at least read_probe_sink_words(bytes) entries")
+    _check("read_probe", lib().read_probe(t.data_ptr(), nbytes, sink.data_ptr(), _stream(t)))
+    return sink
 
 
 def quantize_weight(w):

@@ -147,6 +147,22 @@ int bf16_from_f32(const float* v, int64_t n, uint16_t* y_bf16, hipStream_t strea
   return launch_status(w8a8::launch_convert_bf16(v, n, y_bf16, stream));
 }
 
+int64_t read_probe_sink_words(int64_t bytes) {
+  if (bytes < 0) return 0;
+  return (bytes + w8a8::kProbeBytesPerBlock - 1) / w8a8::kProbeBytesPerBlock;
+}
+
+int read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes < 0) return W8A8_ERR_BAD_SHAPE;
+  if (bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return W8A8_ERR_UNSUPPORTED;
+  if (bytes == 0) return W8A8_OK;
+  if (!p || !sink) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(p) || !aligned16(sink)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_read_probe(p, bytes, sink, stream));
+}
+
 size_t fp8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0 || !mul_ok(M, K)) return 0;
   return (size_t)(align256(M * K) + align256(M * 4));

@@ -384,6 +384,29 @@ __global__ __launch_bounds__(256) void gemm_skinny_q(const uint16_t* __restrict_
   }
 }
 
+// The read floor of the decode weight stream: the launch shape of
+// gemm_skinny (256 threads per 32 KB, each lane's eight 16-byte loads in
+// flight together) with no arithmetic but an XOR of what was read, one
+// word per workgroup so the loads are kept.
+__global__ __launch_bounds__(256) void read_probe(const uint8_t* __restrict__ p, int64_t bytes,
+                                                  uint32_t* __restrict__ sink) {
+  const int64_t base = (int64_t)blockIdx.x * kProbeBytesPerBlock;
+  const auto r = make_rsrc(p + base, bytes - base);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v4i v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    v[u] = buffer_load16(r, (uint32_t)((wave * 8 + u) * 1024 + lane * 16));
+  uint32_t x = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) x ^= (uint32_t)(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
+  __shared__ uint32_t part[4];
+  for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off, 64);
+  if (lane == 0) part[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t run_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -409,6 +432,13 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
     return hipGetLastError();
   }
   return run_tiled<256, 192, 2, 4>(a, sa, w, sw, y, M, N, K, stream);
+}
+
+hipError_t launch_read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  hipLaunchKernelGGL(read_probe, dim3((unsigned)((bytes + kProbeBytesPerBlock - 1) / kProbeBytesPerBlock)), dim3(256),
+                     0, stream, p, bytes, sink);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_gemm_decode(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,

@@ -28,6 +28,12 @@ constexpr int64_t kFusedDecodeMaxM = 32, kFusedDecodeMaxK = 2048;
 hipError_t launch_quant_gemm_decode(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
                                     int64_t N, int64_t K, hipStream_t stream);
 
+// The read floor of the decode weight stream (gemm.hip): every byte of p read
+// in gemm_skinny's launch shape, kProbeBytesPerBlock bytes per 256-thread
+// workgroup; sink gets one XOR word per workgroup.
+constexpr int64_t kProbeBytesPerBlock = 32768;
+hipError_t launch_read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Default maths (w8a16.hip): y[m,n] = bf16(sw[n] * sum_k x[m,k] w[n,k]), x BF16,
 // w E4M3 widened to BF16, BF16 MFMA.
 hipError_t launch_w8a16_gemm(const uint16_t* x, const uint8_t* w, const float* sw, uint16_t* y,
