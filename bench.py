@@ -13,7 +13,9 @@ describes the dominant kernel (the GEMM) against the FP8 MFMA dense peak,
 using HIP event timing of each GEMM launch on the stream it runs on.
 ``decode`` reports the weight-streaming GEMM at M = 8 (and 1, 32) as HBM
 GB/s with a rotation of distinct weight buffers larger than the last-level
-cache. ``cpu_baseline`` is the CPU oracle timed on this host.
+cache, beside the read floor of the same buffers in the same launch
+pattern. ``cpu_baseline`` is the CPU oracle timed on this host on the
+prefill workload; ``cpu_baseline_per_workload`` has it for every workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -653,39 +655,134 @@ def bench_moe_mxfp4(reps=10, warmup=3):
     return out
 
 
-def cpu_baseline(min_seconds=10.0):
-    """The CPU oracle on the full prefill workload (activation quantisation,
-    exact float64 GEMM, BF16 rounding), run back to back on this host until
-    at least ``min_seconds`` have passed (at least once); the figure is the
-    mean per run."""
+def _host_info():
+    """Threads the BLAS pool uses, the CPU model and the BLAS library."""
+    threads, blas = os.cpu_count() or 1, "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            threads = max(i.get("num_threads", 1) for i in pools)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools)
+    except Exception:  # pragma: no cover
+        pass
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return threads, model, blas
+
+
+def _timed(fn, min_seconds, min_runs=3):
+    """Run fn back to back at least min_runs times and until min_seconds have
+    passed; returns (min seconds per run, mean seconds per run, runs)."""
+    times = []
+    t0 = time.perf_counter()
+    while len(times) < min_runs or time.perf_counter() - t0 < min_seconds:
+        t = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t)
+    return min(times), sum(times) / len(times), len(times)
+
+
+def _oracle_quant_rows(x, rows=8192):
+    """oracle.quantize_rows over row chunks on a thread pool (input preparation)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    chunks = [x[i:i + rows] for i in range(0, x.shape[0], rows)]
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as pool:
+        res = list(pool.map(oracle.quantize_rows, chunks))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
+def cpu_baselines(prefill_seconds=5.0):
+    """The CPU oracle timed on this host for every workload, on bounded samples:
+    the full prefill, small and decode layers (quantisation, exact float64
+    GEMM, BF16 rounding), the routed gate/up on 4096 tokens, and 2048 of the
+    16384 tokens of the two-pass routed-expert stack (tokens are independent,
+    so the sample is the same work per token); both routed-expert samples use
+    the two-pass workload's tokens and expert weights. Inputs (and the
+    oracle's own weight quantisation) are prepared untimed. Returns (the prefill entry,
+    all entries by workload)."""
     import numpy as np
 
     import oracle
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads, model, blas = _host_info()
+    base = {"kind": "oracle", "cores": threads, "cpu": model, "blas": blas}
+    out = {}
+
+    def dense(cfg, min_seconds, w=None):
+        d = synth.dense_workload(**cfg, seed=0)
+        qw, sw = w if w is not None else oracle.quantize_rows(synth.bf16_bits_to_f32(d["w"]))[:2]
+        x = synth.bf16_bits_to_f32(d["x"])
+
+        def run():
+            qx, sx, _ = oracle.quantize_rows(x)
+            oracle.w8a8_linear(qx, sx, qw, sw)
+        return _timed(run, min_seconds), (qw, sw)
+
     cfg = synth.DENSE_PREFILL
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    d = synth.dense_workload(**cfg, seed=0)
-    qw, sw, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["w"]))
+    (tmin, tmean, runs), _ = dense(cfg, prefill_seconds)
+    out["prefill_4096x2048->6144"] = dict(base, value=2.0 * M * N * K / tmean / 1e12, unit="TFLOP/s",
+                                           seconds=tmean, seconds_min=tmin, runs=runs,
+                                           tokens_per_s=M / tmean,
+                                           sample=f"full workload: quantise + float64 GEMM + BF16 rounding, "
+                                                  f"{runs} runs back to back ({tmean:.2f} s per run)")
+    cfg = synth.DENSE_SMALL
+    (tmin, tmean, runs), _ = dense(cfg, 1.0)
+    out["small_64x1024->1024"] = dict(base, value=2.0 * cfg["M"] * cfg["N"] * cfg["K"] / tmean / 1e12,
+                                       unit="TFLOP/s", seconds=tmean, seconds_min=tmin, runs=runs,
+                                       sample=f"full workload, {runs} runs")
+    cfg = synth.DENSE_DECODE
+    wdec = None
+    for m in (1, 8, 32):
+        c = dict(cfg, M=m)
+        (tmin, tmean, runs), wdec = dense(c, 1.0, wdec)
+        wbytes = c["N"] * c["K"] + 4 * c["N"]
+        out[f"decode_M{m}_x2048->8192"] = dict(base, value=wbytes / tmean / 1e9, unit="GB/s (weight stream)",
+                                                seconds=tmean, seconds_min=tmin, runs=runs,
+                                                sample=f"full layer (quantise the {m}-token input, float64 GEMM), "
+                                                       f"{runs} runs")
+    # routed experts: the two-pass workload's weights, quantised once by the oracle (untimed)
+    cfg = synth.MOE_TWO_PASS
+    T, H, I, E, k = cfg["T"], cfg["H"], cfg["I"], cfg["E"], cfg["k"]
+    d = synth.moe_workload(**cfg, seed=0)
+    q13, s13 = _oracle_quant_rows(synth.bf16_bits_to_f32(d["w13"].reshape(E * 2 * I, H)))
+    q2, s2 = _oracle_quant_rows(synth.bf16_bits_to_f32(d["w2"].reshape(E * H, I)))
+    q13, s13, q2, s2 = q13.reshape(E, 2 * I, H), s13.reshape(E, 2 * I), q2.reshape(E, H, I), s2.reshape(E, H)
     x = synth.bf16_bits_to_f32(d["x"])
-    runs = 0
-    t0 = time.perf_counter()
-    while True:
-        qx, sx, _ = oracle.quantize_rows(x)
-        oracle.w8a8_linear(qx, sx, qw, sw)
-        runs += 1
-        total = time.perf_counter() - t0
-        if total >= min_seconds:
-            break
-    dt = total / runs
-    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full prefill workload {M}x{K} -> {N}: quantise + float64 GEMM + BF16 rounding, {runs} run{'s' if runs != 1 else ''} "
-                      f"back to back in {total:.1f} s ({dt:.2f} s per run)", "seconds": dt, "runs": runs}
+    Tg = synth.MOE_GATE_UP["T"]
+    gids = d["routes"][0][0][:Tg]
+
+    def gate_up():
+        qx, sx, _ = oracle.quantize_rows(x[:Tg])
+        oracle.grouped_gate_up(qx, sx, gids, q13, s13)
+    tmin, tmean, runs = _timed(gate_up, 0.0, min_runs=1)
+    out["moe_gate_up_T4096"] = dict(base, value=2.0 * Tg * k * 2 * I * H / tmean / 1e12, unit="TFLOP/s",
+                                    seconds=tmean, runs=runs, tokens_per_s=Tg / tmean,
+                                    sample=f"{Tg} tokens of the two-pass workload (the same shapes and "
+                                           "distributions): route, quantise, float64 grouped gate/up, once")
+    ns = 2048
+    routes = [(i[:ns], w[:ns]) for i, w in d["routes"]]
+    tmin, tmean, runs = _timed(lambda: oracle.moe_two_pass(x[:ns], routes, q13, s13, q2, s2), 0.0, min_runs=1)
+    flops = 2 * 2.0 * ns * k * (2 * I * H + H * I)
+    out["moe_two_pass_T16384"] = dict(base, value=flops / tmean / 1e12, unit="TFLOP/s", seconds=tmean, runs=runs,
+                                      tokens_per_s=ns / tmean,
+                                      sample=f"{ns} of the 16384 tokens, both passes (tokens are independent), once")
+    main = dict(out["prefill_4096x2048->6144"])
+    return main, out
 
 
 def main():
@@ -738,10 +835,10 @@ def main():
     if not args.no_default_maths:
         print("[bench] default maths (W8A16)", file=sys.stderr, flush=True)
         dm = bench_default_maths()
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline()
+        cpu, cpu_all = cpu_baselines()
     achieved = pre["gemm_flops"] / (pre["gemm_ms_avg"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -782,6 +879,7 @@ def main():
         "moe_mxfp4": moe_mx,
         "default_maths": dm,
         "cpu_baseline": cpu,
+        "cpu_baseline_per_workload": cpu_all,
     }
     print(json.dumps(line))
 
