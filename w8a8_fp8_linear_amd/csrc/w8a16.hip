@@ -203,6 +203,9 @@ __global__ __launch_bounds__(256) void w8a16_skinny(const uint16_t* __restrict__
   const auto rX = make_rsrc(X, (int64_t)M * K * 2);
   const int r16 = lane & 15, g = lane >> 4;
   const uint32_t wrow = (uint32_t)r16 * (uint32_t)K;
+  // the epilogue's weight scales first, so that their latency overlaps the stream
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (wave == 0 && n0 + 4 * g < N) s = *reinterpret_cast<const float4*>(sw + n0 + 4 * g);
   v4f acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -242,7 +245,6 @@ __global__ __launch_bounds__(256) void w8a16_skinny(const uint16_t* __restrict__
   if (wave != 0) return;
   const int n = n0 + 4 * g;
   if (n >= N) return;
-  const float4 s = *reinterpret_cast<const float4*>(sw + n);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const v4f a = acc[t] + red[0][t][lane] + red[1][t][lane] + red[2][t][lane];
