@@ -398,7 +398,8 @@ int moe_down_combine(const uint8_t* h_q, const float* h_scale, const int32_t* pe
   const int d = check_device();
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
-                                                 out_bf16, y_f32, nullptr, nullptr, T, H, I, E, topk, order, stream));
+                                                 out_bf16, y_f32, nullptr, nullptr, T, H, I, E, topk, order, stream,
+                                                 nullptr));
 }
 
 size_t w8a8_grouped_gemm_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
@@ -529,7 +530,7 @@ int moe_mxfp4_down_combine(const uint8_t* h_q, const uint8_t* h_scale, const int
   if (d != W8A8_OK) return d;
   return launch_status(w8a8::launch_mx_down_combine(h_q, h_scale, perm, offsets, topk_ids, topk_w, w2_q, w2_scale,
                                                     out_bf16, y_f32, out_q, out_scale, T, H, I, E, topk, order,
-                                                    stream));
+                                                    stream, nullptr));
 }
 
 size_t moe_mxfp4_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {

@@ -48,11 +48,14 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
 }
 
 // Sum of a token's valid float32 slot rows at columns c0 .. c0 + 7, in the
-// order j = 0, 1, ... in float32 (deterministic). The k rows of a token are
-// contiguous in y; they are loaded (non-temporal: each byte is read once)
-// before any is added, and a dropped slot's row is read but not used.
-__device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __restrict__ ids, int64_t t,
-                                  int topk, int Eids, int H, int c0, float4& a, float4& b) {
+// order j = 0, 1, ... in float32 (deterministic). Slot t * topk + j's row of
+// y is the slot itself, or slot_row[slot] when slot_row is given (the down
+// projection then wrote its rows in sorted order). The rows are loaded
+// (non-temporal: each byte is read once) before any is added; a dropped
+// slot's row is not used.
+__device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __restrict__ ids,
+                                  const int32_t* __restrict__ slot_row, int64_t t, int topk, int Eids, int H, int c0,
+                                  float4& a, float4& b) {
   a = make_float4(0.f, 0.f, 0.f, 0.f);
   b = a;
   constexpr int kBatch = 8;
@@ -65,9 +68,10 @@ __device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __
       const int64_t slot = t * topk + (j < topk ? j : 0);
       const int id = ids[slot];
       ok[jj] = j < topk && id >= 0 && id < Eids;
-      const v4f* row = reinterpret_cast<const v4f*>(y + slot * H + c0);
-      u[jj] = __builtin_nontemporal_load(row);
-      v[jj] = __builtin_nontemporal_load(row + 1);
+      const int64_t row = !ok[jj] ? 0 : slot_row ? (int64_t)slot_row[slot] : slot;
+      const v4f* src = reinterpret_cast<const v4f*>(y + row * H + c0);
+      u[jj] = __builtin_nontemporal_load(src);
+      v[jj] = __builtin_nontemporal_load(src + 1);
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {

@@ -76,11 +76,13 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
 // y: [T*topk, H] float32 scratch (down_combine_scratch_bytes).
 size_t down_combine_scratch_bytes(int64_t T, int64_t H, int64_t topk);
 // out_q / out_s (both NULL or both set): also quantize_per_token(out).
+// slot_row (may be NULL): [T*topk] int32 scratch; when given, y holds the
+// products in sorted order and slot_row the slot -> row map.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm,
                                const int32_t* offsets, const int32_t* ids, const float* tw,
                                const uint8_t* w2, const float* s2, uint16_t* out, float* y,
                                uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I,
-                               int64_t E, int64_t topk, int order, hipStream_t stream);
+                               int64_t E, int64_t topk, int order, hipStream_t stream, int32_t* slot_row);
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids,
                                   const uint8_t* w13, const float* s13, uint16_t* gu, int32_t* perm,
@@ -107,11 +109,12 @@ hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, 
                                           int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
 
 // y: [T*topk, H] float32 scratch; out_q / out_s (both NULL or both set): also
-// the MXFP4 quantisation of out.
+// the MXFP4 quantisation of out; slot_row as for launch_down_combine.
 hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
                                   uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
-                                  int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream);
+                                  int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream,
+                                  int32_t* slot_row);
 
 size_t mx_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);
 

@@ -240,6 +240,7 @@ struct GroupedArgs {
   float* out_f32;           // GATE_UP_H: h [rows, N / 2]; DOWN_Y: y [slots, N]
   uint32_t* row_amax;       // GATE_UP_H: max |h| bits per output row (cleared by the caller)
   const int32_t* dst_row;   // GATE_UP_H: slot -> output row (NULL: the sorted row itself)
+  int32_t* slot_row;        // DOWN_Y: NULL, y row = slot; else y row = sorted row, and slot_row[slot] = it
   int N, K, tiles_n, tiles_m_max;
 };
 
@@ -260,8 +261,11 @@ struct GroupedArgs {
 //  DOWN_Y:    A row = h codes of sorted row r (contiguous); the epilogue
 //             stores w[slot] * sA[r] * sB[e, n] * acc in float32 to row
 //             `slot` of out_f32 [T * topk, N] (every slot is written once),
-//             straight from registers: a lane holds 4 consecutive columns of
-//             one row, one 16-byte store.
+//             or with slot_row to row r (a tile's rows are then one
+//             contiguous block; the n-tile 0 workgroups record
+//             slot_row[slot] = r for the combine), straight from registers:
+//             a lane holds 4 consecutive columns of one row, one 16-byte
+//             store.
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
@@ -372,7 +376,14 @@ void grouped_tiled(const GroupedArgs p) {
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (K + 127) >> 7;
   issue(0, 0);
-  if (kIsDown) setup_rows();
+  if (kIsDown) {
+    setup_rows();
+    if (p.slot_row != nullptr && nt == 0)
+      for (int i = tid; i < rows; i += C::kThreads) {
+        const int slot = p.perm[row0 + i];
+        if (slot >= 0 && slot < cap) p.slot_row[slot] = row0 + i;
+      }
+  }
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmem_all();
     __syncthreads();
@@ -407,8 +418,9 @@ void grouped_tiled(const GroupedArgs p) {
         const int slot = row_tok[ml];
         const float s = row_scale[ml];
         const v4f a = acc[i][j];
+        const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
-          store16_nt(p.out_f32 + (int64_t)slot * N + n,
+          store16_nt(p.out_f32 + yrow * N + n,
                      make_float4(a[0] * s * sW.x, a[1] * s * sW.y, a[2] * s * sW.z, a[3] * s * sW.w));
       }
     }
@@ -548,7 +560,8 @@ __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, i
 // out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots.
 // One thread per 8 columns.
 __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                                                     int64_t T, int topk, int Eids, int H,
+                                                     const int32_t* __restrict__ slot_row, int64_t T, int topk,
+                                                     int Eids, int H,
                                                      uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int per_row = H >> 3;
@@ -556,7 +569,7 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
   if (t >= T) return;
   const int c0 = (int)(i - t * per_row) << 3;
   float4 a, b;
-  sum_slots8(y, ids, t, topk, Eids, H, c0, a, b);
+  sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
   *reinterpret_cast<uint4*>(out + t * H + c0) = to_bf16x8(a, b);
 }
 
@@ -567,7 +580,7 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
 // fl32(x / s) (the same shared quantiser code).
 template <int PER>
 __global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                                                     int topk, int Eids, int H, uint16_t* __restrict__ out,
+                                                     const int32_t* __restrict__ slot_row, int topk, int Eids, int H, uint16_t* __restrict__ out,
                                                      uint8_t* __restrict__ q, float* __restrict__ qs) {
   __shared__ uint32_t wmax[4];
   const int64_t t = blockIdx.x;
@@ -580,7 +593,7 @@ __global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y
     vb[p] = make_uint4(0u, 0u, 0u, 0u);
     if (c0 < H) {
       float4 a, b;
-      sum_slots8(y, ids, t, topk, Eids, H, c0, a, b);
+      sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
       vb[p] = to_bf16x8(a, b);
       *reinterpret_cast<uint4*>(out + t * H + c0) = vb[p];
       const uint32_t m = absmax8(vb[p]);
@@ -727,12 +740,14 @@ hipError_t launch_gate_up_swiglu_quant(const uint8_t* xq, const float* xs, const
 }
 
 // Down projection of the sorted rows (any order: every slot's product goes
-// to its own row of y), then the per-token combine.
+// to its own row of y, or with slot_row to its sorted row), then the
+// per-token combine.
 hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t* perm, const int32_t* offsets,
                                const int32_t* ids, const float* tw, const uint8_t* w2, const float* s2, uint16_t* out,
                                float* y, uint8_t* out_q, float* out_s, int64_t T, int64_t H, int64_t I, int64_t E,
-                               int64_t topk, int order, hipStream_t stream) {
+                               int64_t topk, int order, hipStream_t stream, int32_t* slot_row) {
   GroupedArgs a{};
+  a.slot_row = slot_row;
   a.A = qh;
   a.sA = sh;
   a.a_rows = T * topk;
@@ -752,15 +767,15 @@ hipError_t launch_down_combine(const uint8_t* qh, const float* sh, const int32_t
   if (out_q != nullptr && H <= 2048 * 4) {
     const dim3 grid((unsigned)T);
     if (H <= 2048)
-      hipLaunchKernelGGL(combine_quant<1>, grid, dim3(256), 0, stream, y, ids, (int)topk, (int)E, (int)H, out, out_q, out_s);
+      hipLaunchKernelGGL(combine_quant<1>, grid, dim3(256), 0, stream, y, ids, slot_row, (int)topk, (int)E, (int)H, out, out_q, out_s);
     else if (H <= 4096)
-      hipLaunchKernelGGL(combine_quant<2>, grid, dim3(256), 0, stream, y, ids, (int)topk, (int)E, (int)H, out, out_q, out_s);
+      hipLaunchKernelGGL(combine_quant<2>, grid, dim3(256), 0, stream, y, ids, slot_row, (int)topk, (int)E, (int)H, out, out_q, out_s);
     else
-      hipLaunchKernelGGL(combine_quant<4>, grid, dim3(256), 0, stream, y, ids, (int)topk, (int)E, (int)H, out, out_q, out_s);
+      hipLaunchKernelGGL(combine_quant<4>, grid, dim3(256), 0, stream, y, ids, slot_row, (int)topk, (int)E, (int)H, out, out_q, out_s);
     return hipGetLastError();
   }
   const int64_t threads = T * (H / 8);
-  hipLaunchKernelGGL(combine_slots, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, y, ids, T,
+  hipLaunchKernelGGL(combine_slots, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, y, ids, slot_row, T,
                      (int)topk, (int)E, (int)H, out);
   if (out_q == nullptr) return hipGetLastError();
   const hipError_t cerr = hipGetLastError();  // rows longer than the fused kernel holds: quantise separately
@@ -818,8 +833,10 @@ hipError_t launch_moe(const uint8_t* xq, const float* xs, const int32_t* ids, co
   err = launch_gate_up_swiglu_quant(xq, xs, perm, offsets, nullptr, w13, s13, qh, sh, nullptr, T, H, I, E, topk, 0,
                                     b + L.amax, stream, true);
   if (err != hipSuccess) return err;
+  // the down projection writes y in sorted order (each tile's rows one
+  // block) and the slot -> row map into the row maxima's words, free by then
   return launch_down_combine(qh, sh, perm, offsets, ids, tw, w2, s2, out, reinterpret_cast<float*>(b + L.big), out_q,
-                             out_s, T, H, I, E, topk, 0, stream);
+                             out_s, T, H, I, E, topk, 0, stream, reinterpret_cast<int32_t*>(b + L.amax));
 }
 
 hipError_t launch_grouped_gate_up(const uint8_t* xq, const float* xs, const int32_t* ids, const uint8_t* w13,

@@ -36,7 +36,8 @@
 //                 registers and stored: no float32 h round trip, no row
 //                 maximum, no atomics, no second kernel;
 //      DOWN_Y     per-slot float32 y = w[slot] * acc, stored straight from
-//                 registers to the slot's own row.
+//                 registers to the slot's own row (or, in the full pass, to
+//                 its sorted row, recording the slot -> row map).
 //  * combine_mx: the ordered per-token slot sum of the FP8 combine (float32
 //    rows and sums, one BF16 rounding), with the BF16 result optionally
 //    quantised to MXFP4 in the same pass (the next pass's expert input).
@@ -168,6 +169,7 @@ struct MxArgs {
   const float* tw;          // DOWN_Y: router weights [slots]
   uint16_t* out_bf16;       // GATE_UP: [rows, N]
   float* out_f32;           // DOWN_Y: y [slots, N]
+  int32_t* slot_row;        // DOWN_Y: NULL, y row = slot; else y row = sorted row, and slot_row[slot] = it
   uint8_t* out_q;           // GATE_UP_Q: h codes [rows, N/4]
   uint8_t* out_s;           // GATE_UP_Q: h scales [rows, N/64]
   const int32_t* dst_row;   // GATE_UP_Q: slot -> output row (NULL: the sorted row)
@@ -309,7 +311,14 @@ void mx_grouped(const MxArgs p) {
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (Kb + 127) >> 7;
   issue(0, 0);
-  if (kIsDown) setup_rows();
+  if (kIsDown) {
+    setup_rows();
+    if (p.slot_row != nullptr && nt == 0)
+      for (int i = tid; i < rows; i += C::kThreads) {
+        const int slot = p.perm[row0 + i];
+        if (slot >= 0 && slot < cap) p.slot_row[slot] = row0 + i;
+      }
+  }
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmem_all();
     __syncthreads();
@@ -358,8 +367,9 @@ void mx_grouped(const MxArgs p) {
         const int slot = row_tok[ml];
         const float w = row_w[ml];
         const v4f a = acc[i][j];
+        const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
-          store16_nt(p.out_f32 + (int64_t)slot * N + n, make_float4(a[0] * w, a[1] * w, a[2] * w, a[3] * w));
+          store16_nt(p.out_f32 + yrow * N + n, make_float4(a[0] * w, a[1] * w, a[2] * w, a[3] * w));
       }
     }
     return;
@@ -437,7 +447,8 @@ void mx_grouped(const MxArgs p) {
 // columns; H % 32 == 0, so a block's four threads form an aligned quad.
 template <bool QUANT>
 __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                                                  int64_t T, int topk, int Eids, int H, uint16_t* __restrict__ out,
+                                                  const int32_t* __restrict__ slot_row, int64_t T, int topk, int Eids,
+                                                  int H, uint16_t* __restrict__ out,
                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int per_row = H >> 3;
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, c
   if (t >= T) return;
   const int c0 = (int)(i - t * per_row) << 3;
   float4 a, b;
-  sum_slots8(y, ids, t, topk, Eids, H, c0, a, b);
+  sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
   const uint4 v = to_bf16x8(a, b);
   *reinterpret_cast<uint4*>(out + t * H + c0) = v;
   if (QUANT) {
@@ -528,8 +539,10 @@ hipError_t launch_mx_gate_up_swiglu_quant(const uint8_t* xq, const uint8_t* xs, 
 hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* ids, const float* tw, const uint8_t* w2, const uint8_t* s2,
                                   uint16_t* out, float* y, uint8_t* out_q, uint8_t* out_s, int64_t T, int64_t H,
-                                  int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream) {
+                                  int64_t I, int64_t E, int64_t topk, int order, hipStream_t stream,
+                                  int32_t* slot_row) {
   MxArgs a{};
+  a.slot_row = slot_row;
   a.A = qh;
   a.sA = sh;
   a.a_rows = T * topk;
@@ -549,18 +562,19 @@ hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const in
   const int64_t threads = T * (H / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (out_q != nullptr)
-    hipLaunchKernelGGL(combine_mx<true>, grid, dim3(256), 0, stream, y, ids, T, (int)topk, (int)E, (int)H, out, out_q,
-                       out_s);
+    hipLaunchKernelGGL(combine_mx<true>, grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E, (int)H,
+                       out, out_q, out_s);
   else
-    hipLaunchKernelGGL(combine_mx<false>, grid, dim3(256), 0, stream, y, ids, T, (int)topk, (int)E, (int)H, out,
-                       nullptr, nullptr);
+    hipLaunchKernelGGL(combine_mx<false>, grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E, (int)H,
+                       out, nullptr, nullptr);
   return hipGetLastError();
 }
 
 // Workspace of the full pass: counts | offsets | perm | route scratch |
-// h codes [T*k, I/2] | h scales [T*k, I/32] | y [T*k, H] float32.
+// h codes [T*k, I/2] | h scales [T*k, I/32] | slot -> row [T*k] |
+// y [T*k, H] float32 (in sorted order).
 struct MxLayout {
-  int64_t counts, offsets, perm, route, qh, sh, y, total;
+  int64_t counts, offsets, perm, route, qh, sh, slot_row, y, total;
 };
 
 static MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
@@ -574,6 +588,7 @@ static MxLayout mx_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t to
   L.route = o; o += (int64_t)route_workspace_bytes(T, topk, E);
   L.qh = o; o += al(n * I / 2);
   L.sh = o; o += al(n * I / 32);
+  L.slot_row = o; o += al(n * 4);
   L.y = o; o += al(n * H * 4);
   L.total = o;
   return L;
@@ -598,7 +613,8 @@ hipError_t launch_mx_moe(const uint8_t* xq, const uint8_t* xs, const int32_t* id
                                        0, stream);
   if (err != hipSuccess) return err;
   return launch_mx_down_combine(b + L.qh, b + L.sh, perm, offsets, ids, tw, w2, s2, out,
-                                reinterpret_cast<float*>(b + L.y), out_q, out_s, T, H, I, E, topk, 0, stream);
+                                reinterpret_cast<float*>(b + L.y), out_q, out_s, T, H, I, E, topk, 0, stream,
+                                reinterpret_cast<int32_t*>(b + L.slot_row));
 }
 
 }  // namespace w8a8
