@@ -77,7 +77,9 @@ class W8A8Error(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree build, or the library named by ``W8A8_LIB`` (for example a
+    host-sanitized build)."""
+    return os.environ.get("W8A8_LIB") or os.path.join(_HERE, _LIB_NAME)
 
 
 def lib() -> ctypes.CDLL:
