@@ -34,7 +34,8 @@
 //      DOWN_Y     A = the requantised rows (sorted, contiguous), B = W2 of
 //                 the tile's expert; the epilogue applies the row scale, the
 //                 channel scale and the router weight and stores the slot's
-//                 float32 product y to its own row.
+//                 float32 product y to its own row (or, in the full pass, to
+//                 its sorted row), staged through LDS into whole row pieces.
 //  * requant_rows: elementwise E4M3 requantisation of h once the row maxima
 //    are known (scale = amax / 448, correctly rounded division, RNE).
 //  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots
@@ -263,9 +264,8 @@ struct GroupedArgs {
 //             `slot` of out_f32 [T * topk, N] (every slot is written once),
 //             or with slot_row to row r (a tile's rows are then one
 //             contiguous block; the n-tile 0 workgroups record
-//             slot_row[slot] = r for the combine), straight from registers:
-//             a lane holds 4 consecutive columns of one row, one 16-byte
-//             store.
+//             slot_row[slot] = r for the combine), staged through LDS so
+//             that every store instruction writes whole row pieces.
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
@@ -403,25 +403,51 @@ void grouped_tiled(const GroupedArgs p) {
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
   if (MODE == kDownY) {
-    // The weighted copy in float32. Each lane's 4 values are consecutive
-    // columns of one row, so the stores go out straight from registers as
-    // 16-byte row pieces (measured faster than staging float32 rows in LDS,
-    // which would also need twice the BF16 staging space).
+    // The weighted copy in float32, staged through LDS (the K loop's stages
+    // are free now) one wm's rows at a time, then written as whole row
+    // pieces: one store instruction covers BN * 4 contiguous bytes of each
+    // of 256 / BN rows. Straight from the MFMA registers an instruction would
+    // cover 16 rows x 64 bytes, which the memory system drains markedly
+    // slower (a plain write stream of each shape: 3.9 against 5.9 TB/s).
+    // Staged rows are XOR-swizzled by 16-byte chunk so that both the
+    // register writes (16 rows per lane group) and the row reads are free of
+    // bank conflicts.
+    constexpr int kChunks = BN / 4;                 // 16-byte chunks of a staged row
+    constexpr int kRowsPerInst = 64 / kChunks;
+    static_assert(C::WM * BN * 4 <= 2 * C::kStage, "a wm's rows must fit in the stages");
+    static_assert(kChunks >= 16 && 64 % kChunks == 0, "row pieces must tile a wave");
+    float4 sW[C::SN];
 #pragma unroll
     for (int i = 0; i < C::SN; ++i) {
       const int n = n0 + wn * C::WN + i * 16 + 4 * g;
-      const float4 sW = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      sW[i] = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int round = 0; round < WGM; ++round) {
+      __syncthreads();  // the stages (round 0) or the previous round's rows are read
+      if (wm == round) {
 #pragma unroll
-      for (int j = 0; j < C::SM; ++j) {
-        const int ml = wm * C::WM + j * 16 + r16;
+        for (int j = 0; j < C::SM; ++j) {
+          const int rl = j * 16 + r16;
+          const float s = row_scale[wm * C::WM + rl];
+#pragma unroll
+          for (int i = 0; i < C::SN; ++i) {
+            const int chunk = wn * (C::WN / 4) + i * 4 + g;
+            const v4f a = acc[i][j];
+            *reinterpret_cast<float4*>(smem + rl * (BN * 4) + ((chunk ^ (rl & 15)) << 4)) =
+                make_float4(a[0] * s * sW[i].x, a[1] * s * sW[i].y, a[2] * s * sW[i].z, a[3] * s * sW[i].w);
+          }
+        }
+      }
+      __syncthreads();
+      const int c = lane % kChunks;
+      const int n = n0 + c * 4;
+      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < C::WM; rl += (C::kThreads / 64) * kRowsPerInst) {
+        const int ml = round * C::WM + rl;
         const int slot = row_tok[ml];
-        const float s = row_scale[ml];
-        const v4f a = acc[i][j];
         const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
           store16_nt(p.out_f32 + yrow * N + n,
-                     make_float4(a[0] * s * sW.x, a[1] * s * sW.y, a[2] * s * sW.z, a[3] * s * sW.w));
+                     *reinterpret_cast<const float4*>(smem + rl * (BN * 4) + ((c ^ (rl & 15)) << 4)));
       }
     }
     return;

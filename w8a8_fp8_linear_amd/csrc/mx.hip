@@ -35,9 +35,10 @@
 //                 block), the exponent and the E2M1 codes are made in
 //                 registers and stored: no float32 h round trip, no row
 //                 maximum, no atomics, no second kernel;
-//      DOWN_Y     per-slot float32 y = w[slot] * acc, stored straight from
-//                 registers to the slot's own row (or, in the full pass, to
-//                 its sorted row, recording the slot -> row map).
+//      DOWN_Y     per-slot float32 y = w[slot] * acc, staged through LDS
+//                 and stored as whole row pieces to the slot's own row (or,
+//                 in the full pass, to its sorted row, recording the
+//                 slot -> row map).
 //  * combine_mx: the ordered per-token slot sum of the FP8 combine (float32
 //    rows and sums, one BF16 rounding), with the BF16 result optionally
 //    quantised to MXFP4 in the same pass (the next pass's expert input).
@@ -356,20 +357,41 @@ void mx_grouped(const MxArgs p) {
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
   if (MODE == kMxDownY) {
-    // y = w * acc in float32, straight from registers: each lane's 4 values
-    // are consecutive columns of one row, one 16-byte store.
+    // y = w * acc in float32, staged through LDS one wm's rows at a time and
+    // written as whole row pieces (BN * 4 contiguous bytes of each of
+    // 256 / BN rows per store instruction), as in the FP8 down projection:
+    // straight from the MFMA registers an instruction covers 16 rows x 64
+    // bytes, which drains markedly slower. 16-byte chunks XOR-swizzled by row.
+    constexpr int kChunks = BN / 4;
+    constexpr int kRowsPerInst = 64 / kChunks;
+    static_assert(C::WM * BN * 4 <= 2 * C::kStage, "a wm's rows must fit in the stages");
+    static_assert(kChunks >= 16 && 64 % kChunks == 0, "row pieces must tile a wave");
+    for (int round = 0; round < WGM; ++round) {
+      __syncthreads();  // the stages (round 0) or the previous round's rows are read
+      if (wm == round) {
 #pragma unroll
-    for (int i = 0; i < C::SN; ++i) {
-      const int n = n0 + wn * C::WN + i * 16 + 4 * g;
+        for (int j = 0; j < C::SM; ++j) {
+          const int rl = j * 16 + r16;
+          const float w = row_w[wm * C::WM + rl];
 #pragma unroll
-      for (int j = 0; j < C::SM; ++j) {
-        const int ml = wm * C::WM + j * 16 + r16;
+          for (int i = 0; i < C::SN; ++i) {
+            const int chunk = wn * (C::WN / 4) + i * 4 + g;
+            const v4f a = acc[i][j];
+            *reinterpret_cast<float4*>(smem + rl * (BN * 4) + ((chunk ^ (rl & 15)) << 4)) =
+                make_float4(a[0] * w, a[1] * w, a[2] * w, a[3] * w);
+          }
+        }
+      }
+      __syncthreads();
+      const int c = lane % kChunks;
+      const int n = n0 + c * 4;
+      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < C::WM; rl += (C::kThreads / 64) * kRowsPerInst) {
+        const int ml = round * C::WM + rl;
         const int slot = row_tok[ml];
-        const float w = row_w[ml];
-        const v4f a = acc[i][j];
         const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
-          store16_nt(p.out_f32 + yrow * N + n, make_float4(a[0] * w, a[1] * w, a[2] * w, a[3] * w));
+          store16_nt(p.out_f32 + yrow * N + n,
+                     *reinterpret_cast<const float4*>(smem + rl * (BN * 4) + ((c ^ (rl & 15)) << 4)));
       }
     }
     return;
