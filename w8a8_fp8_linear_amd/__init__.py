@@ -90,6 +90,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
                                "or python -m w8a8_fp8_linear_amd.build")
+        # torch first: the library then binds to the HIP runtime torch has
+        # loaded (the one its tensors and streams belong to) rather than
+        # bringing in a second copy of the runtime
+        import torch  # noqa: F401
+
         handle = ctypes.CDLL(path)
         for name, (res, args) in _SIGNATURES.items():
             f = getattr(handle, name)
