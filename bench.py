@@ -45,12 +45,12 @@ def _bf16_dev(bits):
 
 
 # HBM bytes per launch of the prefill GEMM kernel, from two rocprofv3 counter
-# passes over `bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-decode
-# --no-moe --copy-calibration` (profiles/gemm_prefill_hbm_counters.md):
-# FETCH_SIZE 41,079 KiB per dispatch, scaled by 2 because the same counter
-# reads 131,093 KiB for the 256 MiB device copy; WRITE_SIZE 49,220 KiB, scale 1
+# passes over `bench.py --steps 5 --warmup 1 --no-default-maths
+# --no-cpu-baseline --copy-calibration` (profiles/gemm_prefill_hbm_counters.md):
+# FETCH_SIZE 41,087 KiB per dispatch, scaled by 2 because the same counter
+# reads 131,094 KiB for the 256 MiB device copy; WRITE_SIZE 49,231 KiB, scale 1
 # (the copy's 262,144 KiB). Valid for this kernel only; None for any other.
-GEMM_PREFILL_TRAFFIC = {"kernel": "gemm_tiled<256,192,2,4>", "bytes": (41079 * 2 + 49220) * 1024}
+GEMM_PREFILL_TRAFFIC = {"kernel": "gemm_tiled<256,192,2,4>", "bytes": (41087 * 2 + 49231) * 1024}
 GEMM_PREFILL_KERNEL = "gemm_tiled<256,192,2,4>"
 
 
