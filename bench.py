@@ -729,7 +729,7 @@ def _oracle_quant_rows(x, rows=8192):
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
 
 
-def cpu_baselines(prefill_seconds=5.0):
+def cpu_baselines(prefill_seconds=10.0):
     """The CPU oracle timed on this host for every workload, on bounded samples:
     the full prefill, small and decode layers (quantisation, exact float64
     GEMM, BF16 rounding), the routed gate/up on 4096 tokens, and 2048 of the
