@@ -242,10 +242,10 @@ int fp8_linear_single_launch(const uint16_t* x_bf16, const uint8_t* w_q, const f
  * model maps onto SGLang"). Readings taken where the pages are silent:
  * W13[e] holds [gate; up] rows; h = silu(g) * u in float32; h is requantised
  * with one E4M3 scale per routed copy; each routed copy's output, weighted
- * by its router weight, is rounded to BF16 (the model's dtype between the
- * expert stage and the top-k sum, as in the fused-MoE kernels the model is
- * built on: sglang-metis 0.1.0, the package description); the k BF16
- * outputs of a token are summed in float32 and rounded once to BF16.
+ * by its router weight, stays in float32 (no page puts a rounding between
+ * the experts and the top-k sum: Lernex/Metis-1.6-Logos-FP8, "What is in
+ * FP8"); the k weighted copies of a token are summed in float32 in the
+ * order j = 0, 1, ... and rounded once to BF16.
  *
  * Shapes (all row-major)
  *   x_q      [T, H]       E4M3 tokens, quantised once per token (quantize_per_token)
@@ -405,9 +405,9 @@ int moe_w8a8_grouped(const uint8_t* x_q, const float* x_scale, const int32_t* to
  *
  * The expert chain is that of the FP8 calls above with every expert input
  * and weight in MXFP4: tokens are quantised once over H, h = silu(g) * u
- * (float32) is quantised per routed copy over I, y = bf16(topk_w * product),
- * and the k BF16 outputs of a token are summed in float32 in the order
- * j = 0, 1, ... and rounded once to BF16.
+ * (float32) is quantised per routed copy over I, y = topk_w * product in
+ * float32, and the k weighted copies of a token are summed in float32 in the
+ * order j = 0, 1, ... and rounded once to BF16.
  * Shapes: x_q [T, H/2] / x_scale [T, H/32]; w13_q [E, 2I, H/2] /
  * w13_scale [E, 2I, H/32] (rows 0..I-1 gate, I..2I-1 up); w2_q [E, H, I/2] /
  * w2_scale [E, H, I/32]; h_q [T*topk, I/2] / h_scale [T*topk, I/32].
