@@ -422,9 +422,9 @@ void grouped_tiled(const GroupedArgs p) {
       const int n = n0 + wn * C::WN + i * 16 + 4 * g;
       sW[i] = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int round = 0; round < WGM; ++round) {
-      __syncthreads();  // the stages (round 0) or the previous round's rows are read
-      if (wm == round) {
+    for (int pass = 0; pass < WGM; ++pass) {
+      __syncthreads();  // the K-loop stages (pass 0) or the previous pass's rows are read
+      if (wm == pass) {
 #pragma unroll
         for (int j = 0; j < C::SM; ++j) {
           const int rl = j * 16 + r16;
@@ -442,7 +442,7 @@ void grouped_tiled(const GroupedArgs p) {
       const int c = lane % kChunks;
       const int n = n0 + c * 4;
       for (int rl = wave * kRowsPerInst + lane / kChunks; rl < C::WM; rl += (C::kThreads / 64) * kRowsPerInst) {
-        const int ml = round * C::WM + rl;
+        const int ml = pass * C::WM + rl;
         const int slot = row_tok[ml];
         const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)

@@ -366,9 +366,9 @@ void mx_grouped(const MxArgs p) {
     constexpr int kRowsPerInst = 64 / kChunks;
     static_assert(C::WM * BN * 4 <= 2 * C::kStage, "a wm's rows must fit in the stages");
     static_assert(kChunks >= 16 && 64 % kChunks == 0, "row pieces must tile a wave");
-    for (int round = 0; round < WGM; ++round) {
-      __syncthreads();  // the stages (round 0) or the previous round's rows are read
-      if (wm == round) {
+    for (int pass = 0; pass < WGM; ++pass) {
+      __syncthreads();  // the K-loop stages (pass 0) or the previous pass's rows are read
+      if (wm == pass) {
 #pragma unroll
         for (int j = 0; j < C::SM; ++j) {
           const int rl = j * 16 + r16;
@@ -386,7 +386,7 @@ void mx_grouped(const MxArgs p) {
       const int c = lane % kChunks;
       const int n = n0 + c * 4;
       for (int rl = wave * kRowsPerInst + lane / kChunks; rl < C::WM; rl += (C::kThreads / 64) * kRowsPerInst) {
-        const int ml = round * C::WM + rl;
+        const int ml = pass * C::WM + rl;
         const int slot = row_tok[ml];
         const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
