@@ -346,6 +346,41 @@ def _oracle_pass_tokens(qx, sx, ids, w, d, tokens):
     return out64
 
 
+def _check_pass_stagewise(d, dv, qx_ref, sx_ref, xq, xs, ids, tw, full_out, tokens):
+    """One routed-expert pass checked stage by stage on ``tokens``, each stage
+    fed the GPU's own input of that stage: the full pass's BF16 output must
+    equal the stage-by-stage chain (route, gate/up + SwiGLU + requant, down +
+    combine) bit for bit; h inside its propagated bound; the requantised codes
+    bit-exact on the GPU's h; the down projection + combine inside the element
+    bound. ``dv`` holds the device copies of the weights (``_dev``). Returns
+    (chain output, its bits, down+combine report, requant report)."""
+    ids_d, tw_d = to_dev(ids), to_dev(tw)
+    _, off, perm = w8.moe_route(ids_d, d["E"])
+    hq, hs, h = w8.moe_gate_up_swiglu_quant(xq, xs, perm, off, dv["q13"], dv["s13"], d["k"], return_h=True)
+    out = w8.moe_down_combine(hq, hs, perm, off, ids_d, tw_d, dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    out_bits = bf16_bits(out)
+    assert np.array_equal(out_bits, bf16_bits(full_out)), "the full pass differs from the stage-by-stage chain"
+    _, _, rp = oracle.route(ids, d["E"])
+    inv = np.full(ids.size, -1, np.int64)
+    inv[rp] = np.arange(rp.size)
+    rows = np.sort(inv[(tokens[:, None] * d["k"] + np.arange(d["k"])[None, :]).reshape(-1)])
+    rows = rows[rows >= 0]
+    h_gpu = h.cpu().numpy()[rows]
+    q_ref, s_ref, _ = oracle.quantize_rows(h_gpu)
+    assert np.array_equal(hq.cpu().numpy()[rows], q_ref)
+    assert np.array_equal(hs.cpu().numpy()[rows].view(np.uint32), s_ref.view(np.uint32))
+    gu64, err = sorted_rows_gate_up(qx_ref, sx_ref, ids, rp, rows, d["q13"], d["s13"], d["k"])
+    h32, dh = swiglu_bound(gu64, err)
+    assert not (np.abs(h_gpu.astype(np.float64) - h32) > dh).any(), "h outside its bound"
+    rq = check_requant(hq.cpu().numpy()[rows], hs.cpu().numpy()[rows], gu64, err)
+    ref64, derr = down_combine_ref(hq.cpu().numpy(), hs.cpu().numpy(), perm.cpu().numpy(), ids, tw,
+                                   d["q2"], d["s2"], d["k"], tokens)
+    rep_dc = bf16_compare(out_bits[tokens], ref64, derr)
+    assert rep_dc["n_bound_violations"] == 0, rep_dc
+    return out, out_bits, rep_dc, rq
+
+
 @pytest.mark.parametrize("cfg", ["small", "ragged", "mid"])
 def test_full_pass_small(cfg, request):
     d = request.getfixturevalue(cfg)
@@ -353,8 +388,13 @@ def test_full_pass_small(cfg, request):
     ids, w = d["routes"][0]
     out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
     torch.cuda.synchronize()
-    ref64 = _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, np.arange(d["T"]))
+    tokens = np.arange(d["T"])
+    _, _, rep_dc, rq = _check_pass_stagewise(d, dv, d["qx"], d["sx"], dv["qx"], dv["sx"], ids, w, out, tokens)
+    ref64 = _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, tokens)
     rep = bf16_compare(bf16_bits(out), ref64)
+    rep.update({"down_combine_frobenius": rep_dc["frobenius"], "down_combine_max_abs_over_rms":
+                rep_dc["max_abs_over_rms"], "requant_codes_differ_from_oracle": rq["n_codes_differ"],
+                "requant_codes": rq["n"]})
     print(f"full pass {cfg}", rep, flush=True)
     record(f"moe full pass {cfg} T={d['T']} H={d['H']} I={d['I']} E={d['E']} k={d['k']}", rep)
     assert rep["frobenius"] <= 4e-3, rep
@@ -387,31 +427,7 @@ def test_two_pass_stack(two_pass_cfg):
         # the token codes of this pass's input
         qx_ref, sx_ref, _ = oracle.quantize_rows(oracle.bf16_bits_to_f64(x_bits).astype(np.float32))
         assert np.array_equal(xq.cpu().numpy(), qx_ref) and np.array_equal(xs.cpu().numpy(), sx_ref)
-        _, off, perm = w8.moe_route(ids_d, d["E"])
-        hq, hs, h = w8.moe_gate_up_swiglu_quant(xq, xs, perm, off, dv["q13"], dv["s13"], d["k"], return_h=True)
-        out = w8.moe_down_combine(hq, hs, perm, off, ids_d, tw_d, dv["q2"], dv["s2"])
-        torch.cuda.synchronize()
-        out_bits = bf16_bits(out)
-        assert np.array_equal(out_bits, bf16_bits(outs[p])), "moe_ffn differs from the stage-by-stage chain"
-        # h and its requantisation on the sampled tokens' slots
-        _, _, rp = oracle.route(ids, d["E"])
-        inv = np.full(ids.size, -1, np.int64)
-        inv[rp] = np.arange(rp.size)
-        rows = np.sort(inv[(tokens[:, None] * d["k"] + np.arange(d["k"])[None, :]).reshape(-1)])
-        rows = rows[rows >= 0]
-        h_gpu = h.cpu().numpy()[rows]
-        q_ref, s_ref, _ = oracle.quantize_rows(h_gpu)
-        assert np.array_equal(hq.cpu().numpy()[rows], q_ref)
-        assert np.array_equal(hs.cpu().numpy()[rows].view(np.uint32), s_ref.view(np.uint32))
-        gu64, err = sorted_rows_gate_up(qx_ref, sx_ref, ids, rp, rows, d["q13"], d["s13"], d["k"])
-        h32, dh = swiglu_bound(gu64, err)
-        assert not (np.abs(h_gpu.astype(np.float64) - h32) > dh).any(), "h outside its bound"
-        rq = check_requant(hq.cpu().numpy()[rows], hs.cpu().numpy()[rows], gu64, err)
-        # down projection + combine from the GPU's codes: element bound
-        ref64, derr = down_combine_ref(hq.cpu().numpy(), hs.cpu().numpy(), perm.cpu().numpy(), ids, tw,
-                                       d["q2"], d["s2"], d["k"], tokens)
-        rep_dc = bf16_compare(out_bits[tokens], ref64, derr)
-        assert rep_dc["n_bound_violations"] == 0, rep_dc
+        out, out_bits, rep_dc, rq = _check_pass_stagewise(d, dv, qx_ref, sx_ref, xq, xs, ids, tw, outs[p], tokens)
         # end to end against the oracle's pass from the same input
         ref_e2e = _oracle_pass_tokens(qx_ref, sx_ref, ids, tw, d, tokens)
         rep = bf16_compare(out_bits[tokens], ref_e2e)
@@ -495,16 +511,21 @@ def test_fused_output_quantisation(cfg):
 @pytest.mark.parametrize("E", [128, 192])
 def test_pages_expert_shapes(E):
     """The model pages' expert shapes (128 or 192 experts, latent width 1024,
-    top-4; the intermediate width 512 is a reading): a full pass against the
-    oracle on every token, 512 tokens."""
+    top-4; the intermediate width 512 is a reading): a full pass on 512
+    tokens, checked stage by stage and end to end against the oracle on
+    every token."""
     print(f"[pages shape] E={E}", flush=True)
     d = quantized_moe(T=512, H=1024, I=512, E=E, k=4, n_outlier=5, seed=E)
     dv = _dev(d)
     ids, w = d["routes"][0]
     out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
     torch.cuda.synchronize()
-    ref64 = _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, np.arange(d["T"]))
+    tokens = np.arange(d["T"])
+    _, _, rep_dc, rq = _check_pass_stagewise(d, dv, d["qx"], d["sx"], dv["qx"], dv["sx"], ids, w, out, tokens)
+    ref64 = _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, tokens)
     rep = bf16_compare(bf16_bits(out), ref64)
+    rep.update({"down_combine_frobenius": rep_dc["frobenius"], "requant_codes_differ_from_oracle":
+                rq["n_codes_differ"], "requant_codes": rq["n"]})
     print(f"pages shape E={E}", rep, flush=True)
     record(f"moe full pass pages shape T=512 H=1024 I=512 E={E} k=4", rep)
     assert rep["frobenius"] <= 4e-3, rep
