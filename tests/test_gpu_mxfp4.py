@@ -249,6 +249,16 @@ def _oracle_tokens(x32, ids, w, d, tokens):
     return out64
 
 
+def _check_full_pass_stagewise(d, out):
+    """The full pass equals the stage-by-stage chain bit for bit, and each
+    stage of that chain is checked element by element on every slot and token
+    (the fused h quantisation by the explainable rule, the down projection +
+    combine inside the element bound)."""
+    hq, hs, perm, offsets = _check_fused(d)
+    chain = _check_down(d, hq, hs, perm, offsets)
+    assert np.array_equal(bf16_bits(chain), bf16_bits(out)), "the full pass differs from the stage-by-stage chain"
+
+
 @pytest.mark.parametrize("cfg", ["small", "ragged", "mid"])
 def test_full_pass(cfg, request):
     d = request.getfixturevalue(cfg)
@@ -256,6 +266,7 @@ def test_full_pass(cfg, request):
     ids, w = d["routes"][0]
     out = w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
     torch.cuda.synchronize()
+    _check_full_pass_stagewise(d, out)
     rep = bf16_compare(bf16_bits(out), _oracle_tokens(d["x32"], ids, w, d, np.arange(d["T"])))
     print(f"mx full pass {cfg}", rep, flush=True)
     record(f"mxfp4 full pass {cfg} T={d['T']} H={d['H']} I={d['I']} E={d['E']} k={d['k']}", rep)
@@ -283,13 +294,15 @@ def test_fused_output_quantisation(cfg):
 @pytest.mark.parametrize("E", [128, 192])
 def test_pages_expert_shapes(E):
     """128 or 192 experts, latent width 1024, top-4 (intermediate width 512 is a
-    reading): a full pass against the oracle on every token, 512 tokens."""
+    reading): a full pass on 512 tokens, checked stage by stage and end to end
+    against the oracle on every token."""
     print(f"[mx pages shape] E={E}", flush=True)
     d = quantized_mx_moe(T=512, H=1024, I=512, E=E, k=4, n_outlier=5, seed=E)
     dv = _dev(d)
     ids, w = d["routes"][0]
     out = w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
     torch.cuda.synchronize()
+    _check_full_pass_stagewise(d, out)
     rep = bf16_compare(bf16_bits(out), _oracle_tokens(d["x32"], ids, w, d, np.arange(d["T"])))
     print(f"mx pages shape E={E}", rep, flush=True)
     record(f"mxfp4 full pass pages shape T=512 H=1024 I=512 E={E} k=4", rep)
@@ -344,7 +357,7 @@ def test_large_groups(cfg, order):
     assert cfg["T"] * cfg["k"] // groups >= MX_LARGE_TILE_MIN_ROWS
     d = quantized_mx_moe(**cfg, seed=23)
     hq, hs, perm, offsets = _check_fused(d, order, order, sample=2048)
-    _check_down(d, hq, hs, perm, offsets, order=order, n_tokens=min(512, d["T"]))
+    chain = _check_down(d, hq, hs, perm, offsets, order=order, n_tokens=min(512, d["T"]))
     if order == 0:
         _check_gate_up_bf16(d)
         dv = _dev(d)
@@ -352,6 +365,7 @@ def test_large_groups(cfg, order):
         out = w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"],
                                    dv["s2"])
         torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(chain), bf16_bits(out)), "the full pass differs from the stage chain"
         tokens = np.sort(np.random.default_rng(5).choice(d["T"], min(256, d["T"]), replace=False))
         rep = bf16_compare(bf16_bits(out)[tokens], _oracle_tokens(d["x32"], ids, w, d, tokens))
         record(f"mxfp4 full pass large groups T={d['T']} H={d['H']} I={d['I']} E={d['E']} k={d['k']}", rep)
