@@ -53,3 +53,24 @@ def test_noalloc_size_limit():
     with pytest.raises(w8.W8A8Error) as e:
         w8.fp8_linear_noalloc(x, wq, ws)
     assert e.value.status == 8
+
+
+def test_noalloc_at_the_scratch_limit():
+    """The largest input the scratch holds: 16368 x 4096 codes (align256 of
+    M*K) and 16368 scales (align256 of 4*M) fill the 64 MiB array to its last
+    byte; bit for bit against fp8_linear. One row more is refused."""
+    K, N = 4096, 48
+    limit = int(w8.lib().fp8_linear_noalloc_max_bytes())
+    M = 16368
+    assert int(w8.lib().fp8_linear_workspace_bytes(M, K)) == limit
+    assert int(w8.lib().fp8_linear_workspace_bytes(M + 1, K)) > limit
+    print(f"[noalloc] M={M} K={K} at the scratch limit", flush=True)
+    x, wq, ws = _layer(M, N, K, 3)
+    ref = w8.fp8_linear(x, wq, ws)
+    got = w8.fp8_linear_noalloc(x, wq, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(got), bf16_bits(ref))
+    x1 = torch.zeros((M + 1, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(w8.W8A8Error) as e:
+        w8.fp8_linear_noalloc(x1, wq, ws)
+    assert e.value.status == 8
