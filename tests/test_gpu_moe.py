@@ -458,6 +458,28 @@ def test_all_slots_dropped_gives_zeros(small):
     assert not bf16_bits(out).any()
 
 
+def test_partly_dropped_slots(ragged):
+    """Some slots dropped (id -1, or an id outside [0, E)), the rest routed:
+    the full pass skips exactly those copies. Checked against the oracle's
+    pass on every token and against the stage chain bit for bit; every
+    token with no valid slot left comes out zero."""
+    d = dict(ragged)
+    ids, w = d["routes"][0]
+    ids = ids.copy()
+    ids[::3, 0] = -1
+    ids[1::5, -1] = d["E"] + 2
+    ids[7] = -1                                   # one token with no valid slot
+    d["routes"] = [(ids, w)] + list(d["routes"][1:])
+    dv = _dev(d)
+    out = w8.moe_w8a8_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    tokens = np.arange(d["T"])
+    _check_pass_stagewise(d, dv, d["qx"], d["sx"], dv["qx"], dv["sx"], ids, w, out, tokens)
+    rep = bf16_compare(bf16_bits(out), _oracle_pass_tokens(d["qx"], d["sx"], ids, w, d, tokens))
+    assert rep["frobenius"] <= 4e-3, rep
+    assert not bf16_bits(out)[7].any()
+
+
 def test_moe_argument_errors(small):
     dv = _dev(small)
     ids = torch.zeros((small["T"], small["k"]), dtype=torch.int32, device="cuda")

@@ -411,6 +411,26 @@ def test_all_slots_dropped_gives_zeros(small):
     assert not bf16_bits(out).any()
 
 
+def test_partly_dropped_slots(ragged):
+    """Some slots dropped (id -1, or an id outside [0, E)): the full pass against
+    the oracle on every token and against the stage chain bit for bit; a token
+    with no valid slot left comes out zero."""
+    d = dict(ragged)
+    ids, w = d["routes"][0]
+    ids = ids.copy()
+    ids[::3, 0] = -1
+    ids[1::5, -1] = d["E"] + 2
+    ids[7] = -1
+    d["routes"] = [(ids, w)] + list(d["routes"][1:])
+    dv = _dev(d)
+    out = w8.moe_mxfp4_grouped(dv["qx"], dv["sx"], to_dev(ids), to_dev(w), dv["q13"], dv["s13"], dv["q2"], dv["s2"])
+    torch.cuda.synchronize()
+    _check_full_pass_stagewise(d, out)
+    rep = bf16_compare(bf16_bits(out), _oracle_tokens(d["x32"], ids, w, d, np.arange(d["T"])))
+    assert rep["frobenius"] <= 4e-3, rep
+    assert not bf16_bits(out)[7].any()
+
+
 @pytest.mark.parametrize("cfg", [dict(T=1, H=128, I=128, E=1, k=1), dict(T=3, H=128, I=128, E=2, k=2),
                                  dict(T=70, H=8192, I=128, E=3, k=2), dict(T=40, H=128, I=2048, E=4, k=3)])
 def test_edge_shapes_full_pass(cfg):
