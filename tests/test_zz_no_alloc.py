@@ -74,3 +74,26 @@ def test_noalloc_at_the_scratch_limit():
     with pytest.raises(w8.W8A8Error) as e:
         w8.fp8_linear_noalloc(x1, wq, ws)
     assert e.value.status == 8
+
+
+def test_noalloc_in_a_hip_graph():
+    """The callers this entry point is for: captured once into a HIP graph and
+    replayed three times; before each replay an eager call on another input
+    overwrites the shared scratch. Every replay must equal fp8_linear bit for
+    bit (the captured quantisation rewrites the scratch it then reads)."""
+    x, wq, ws = _layer(300, 1040, 1024, 4)
+    x2, _, _ = _layer(700, 1040, 1024, 5)
+    ref = bf16_bits(w8.fp8_linear(x, wq, ws))
+    out = torch.empty((300, 1040), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty((700, 1040), dtype=torch.bfloat16, device="cuda")
+    w8.fp8_linear_noalloc(x, wq, ws, out=out)  # eager first: the scratch address is looked up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.fp8_linear_noalloc(x, wq, ws, out=out)
+    for i in range(3):
+        out.zero_()
+        w8.fp8_linear_noalloc(x2, wq, ws, out=out2)   # eager work that overwrites the scratch
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(out), ref), f"replay {i} differs"
