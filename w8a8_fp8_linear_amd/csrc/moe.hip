@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
 
 enum { kGateUp = 0, kGateUpH = 1, kDownY = 2 };
 
-template <int BM, int BN, int WGM, int WGN, int MODE>
+template <int BM, int BN, int WGM, int WGN, int MODE, int NS>
 struct Grouped {
   static constexpr int kThreads = 64 * WGM * WGN;
   static constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wave tile
@@ -220,7 +220,11 @@ struct Grouped {
   static constexpr int kLoadsB = BN / kRowsPerPass, kLoadsA = BM / kRowsPerPass;
   static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP)
   static constexpr int kEpi = MODE == kGateUp ? BM * kEpiStride : 0;
-  static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
+  static constexpr int kLds = (NS * kStage > kEpi) ? NS * kStage : kEpi;
+  // The down epilogue stages a wave row block's float32 rows in kJH parts,
+  // each no larger than the K loop's stages.
+  static constexpr int kJH = (MODE == kDownY && WM * BN * 4 > kLds) ? 2 : 1;
+  static_assert(NS == 1 || NS == 2, "one or two stages");
   static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
   static_assert(kRowsPerPass % 8 == 0, "the loader's chunk swizzle needs 8-row passes");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
@@ -248,7 +252,11 @@ struct GroupedArgs {
 // Grouped GEMM over sorted slots: M = sorted rows, N = output columns of the
 // group's expert weight [N, K], K = reduction. Same pipeline as the dense
 // tiled kernel (WGM x WGN waves, 128-deep K steps staged global -> LDS by
-// direct buffer loads, double-buffered, 16x16x128 E4M3 MFMAs).
+// direct buffer loads, 16x16x128 E4M3 MFMAs). NS = 2: two stages, the next
+// step loads into one while the MFMAs read the other. NS = 1: one stage,
+// half the LDS so that more workgroups fit on a CU; each wave takes the
+// step's fragments into registers, the workgroup meets, and the next step's
+// loads then overlap the MFMAs.
 //  GATE_UP:   A row = x[perm[r] / topk] (gathered); out = BF16 [r, N] with the
 //             scales x_scale[token] * sB[e, n].
 //  GATE_UP_H: as GATE_UP, but the stage's weight rows alternate a block of 16
@@ -266,10 +274,10 @@ struct GroupedArgs {
 //             contiguous block; the n-tile 0 workgroups record
 //             slot_row[slot] = r for the combine), staged through LDS so
 //             that every store instruction writes whole row pieces.
-template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void grouped_tiled(const GroupedArgs p) {
-  using C = Grouped<BM, BN, WGM, WGN, MODE>;
+  using C = Grouped<BM, BN, WGM, WGN, MODE, NS>;
   // One LDS object: the stages (or the epilogue's staging), then the row
   // tables. With a single object the compiler does not make the LDS reads
   // of a K step wait for the next step's direct-to-LDS loads.
@@ -387,24 +395,38 @@ void grouped_tiled(const GroupedArgs p) {
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmem_all();
     __syncthreads();
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
-    const uint8_t* st = smem + (kt & 1) * C::kStage;
+    if (NS == 2 && kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
+    const uint8_t* st = smem + (NS == 2 ? (kt & 1) * C::kStage : 0);
     v8i xf[C::SM];
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) xf[j] = lds_frag(st, BN + wm * C::WM + j * 16 + r16, g);
+    if (NS == 1) {
+      // one stage: every fragment of this step in registers, then the next
+      // step's loads, which overlap this step's MFMAs
+      v8i wfa[C::SN];
 #pragma unroll
-    for (int i = 0; i < C::SN; ++i) {
-      const v8i wf = lds_frag(st, wn * C::WN + i * 16 + r16, g);
+      for (int i = 0; i < C::SN; ++i) wfa[i] = lds_frag(st, wn * C::WN + i * 16 + r16, g);
+      lds_barrier();
+      if (kt + 1 < nk) issue(0, (kt + 1) << 7);
 #pragma unroll
-      for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf, xf[j], acc[i][j]);
+      for (int i = 0; i < C::SN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wfa[i], xf[j], acc[i][j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::SN; ++i) {
+        const v8i wf = lds_frag(st, wn * C::WN + i * 16 + r16, g);
+#pragma unroll
+        for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_e4m3(wf, xf[j], acc[i][j]);
+      }
     }
   }
 
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
-  if (MODE == kDownY) {
+  if constexpr (MODE == kDownY) {
     // The weighted copy in float32, staged through LDS (the K loop's stages
-    // are free now) one wm's rows at a time, then written as whole row
+    // are free now) one wm's rows (or half of them) at a time, then written as whole row
     // pieces: one store instruction covers BN * 4 contiguous bytes of each
     // of 256 / BN rows. Straight from the MFMA registers an instruction would
     // cover 16 rows x 64 bytes, which the memory system drains markedly
@@ -414,7 +436,8 @@ void grouped_tiled(const GroupedArgs p) {
     // bank conflicts.
     constexpr int kChunks = BN / 4;                 // 16-byte chunks of a staged row
     constexpr int kRowsPerInst = 64 / kChunks;
-    static_assert(C::WM * BN * 4 <= 2 * C::kStage, "a wm's rows must fit in the stages");
+    constexpr int kJH = C::kJH, kPartRows = C::WM / kJH, kPartJ = C::SM / kJH;
+    static_assert(kPartRows * BN * 4 <= C::kLds && C::SM % kJH == 0, "a part of a wm's rows must fit in the LDS");
     static_assert(kChunks >= 16 && 64 % kChunks == 0, "row pieces must tile a wave");
     float4 sW[C::SN];
 #pragma unroll
@@ -422,13 +445,16 @@ void grouped_tiled(const GroupedArgs p) {
       const int n = n0 + wn * C::WN + i * 16 + 4 * g;
       sW[i] = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int pass = 0; pass < WGM; ++pass) {
-      __syncthreads();  // the K-loop stages (pass 0) or the previous pass's rows are read
-      if (wm == pass) {
 #pragma unroll
-        for (int j = 0; j < C::SM; ++j) {
-          const int rl = j * 16 + r16;
-          const float s = row_scale[wm * C::WM + rl];
+    for (int pass = 0; pass < WGM * kJH; ++pass) {
+      const int pw = pass / kJH, ph = pass % kJH;
+      __syncthreads();  // the K-loop stages (pass 0) or the previous pass's rows are read
+      if (wm == pw) {
+#pragma unroll
+        for (int jl = 0; jl < kPartJ; ++jl) {
+          const int j = ph * kPartJ + jl;
+          const int rl = jl * 16 + r16;
+          const float s = row_scale[wm * C::WM + j * 16 + r16];
 #pragma unroll
           for (int i = 0; i < C::SN; ++i) {
             const int chunk = wn * (C::WN / 4) + i * 4 + g;
@@ -441,8 +467,8 @@ void grouped_tiled(const GroupedArgs p) {
       __syncthreads();
       const int c = lane % kChunks;
       const int n = n0 + c * 4;
-      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < C::WM; rl += (C::kThreads / 64) * kRowsPerInst) {
-        const int ml = pass * C::WM + rl;
+      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < kPartRows; rl += (C::kThreads / 64) * kRowsPerInst) {
+        const int ml = pw * C::WM + ph * kPartRows + rl;
         const int slot = row_tok[ml];
         const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
@@ -655,7 +681,12 @@ constexpr int kDnBM = 256, kDnBN = 256, kDnWGM = 2, kDnWGN = 4, kDnOcc = 2;
 // take smaller tiles: with 256-row tiles much of each group's last tile
 // would be padding, and a pass has too few tiles to fill the chip. Below
 // kSmallGroupRows rows on average: 128 x 128 tiles of 2 x 2 waves; below
-// kTinyGroupRows: 64 x 128 tiles of 1 x 2 waves (three workgroups per CU).
+// kTinyGroupRows: 64 x 128 tiles of 1 x 2 waves. Both with one LDS stage
+// (NS = 1) and up to three waves per SIMD: six 64 x 128 workgroups fit on a
+// CU instead of three, and three 128 x 128 ones instead of two. Against the
+// double-buffered form with its lower occupancy, the same results bit for
+// bit: 7-10% less time for a whole two-pass FFN at 128 and 192 experts, and
+// 3.5% at 4096 tokens, top-8 of 64.
 // Timed at 4096 tokens with 128 and 192 experts (128 and 85 rows per group),
 // at 8192 and 12288 tokens with 128 experts (256 and 384 rows) against
 // 128 x 256, 64 x 256, 64 x 64 and 4-wave 64 x 128 tiles, and at 4096
@@ -664,13 +695,13 @@ constexpr int kDnBM = 256, kDnBN = 256, kDnWGM = 2, kDnWGN = 4, kDnOcc = 2;
 constexpr int64_t kSmallGroupRows = 1024, kTinyGroupRows = 192;
 
 
-template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC, int NS = 2>
 hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles_m_max = (int)((max_rows + BM - 1) / BM + a.G);  // every group adds at most one partial tile
   const int64_t blocks = (int64_t)a.tiles_m_max * a.tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_tiled<BM, BN, WGM, WGN, MODE, OCC>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
+  hipLaunchKernelGGL((grouped_tiled<BM, BN, WGM, WGN, MODE, OCC, NS>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -678,8 +709,8 @@ hipError_t run_grouped(GroupedArgs a, int64_t max_rows, hipStream_t stream) {
 // One grouped launch in the tile shape that suits the average group size.
 template <int MODE>
 hipError_t run_grouped_auto(const GroupedArgs& a, int64_t max_rows, int64_t avg_rows, hipStream_t stream) {
-  if (avg_rows < kTinyGroupRows) return run_grouped<64, 128, 1, 2, MODE, 2>(a, max_rows, stream);
-  if (avg_rows < kSmallGroupRows) return run_grouped<128, 128, 2, 2, MODE, 2>(a, max_rows, stream);
+  if (avg_rows < kTinyGroupRows) return run_grouped<64, 128, 1, 2, MODE, 3, 1>(a, max_rows, stream);
+  if (avg_rows < kSmallGroupRows) return run_grouped<128, 128, 2, 2, MODE, 3, 1>(a, max_rows, stream);
   if (MODE == kDownY) return run_grouped<kDnBM, kDnBN, kDnWGM, kDnWGN, MODE, kDnOcc>(a, max_rows, stream);
   return run_grouped<kGuBM, kGuBN, kGuWGM, kGuWGN, MODE, kGuOcc>(a, max_rows, stream);
 }

@@ -23,7 +23,9 @@
 //  * mx_grouped: the grouped expert pipeline with 256-deep K steps: per row
 //    and stage, 128 bytes of codes (staged and swizzled as in the FP8
 //    kernel) and the row's 8 scale bytes, both by direct buffer -> LDS
-//    loads, double-buffered. A stage is two 16x16x128 FP4 MFMAs per tile
+//    loads, double-buffered (NS = 2) or, for the smallest tiles, in one
+//    stage (NS = 1) that the next step's loads refill while the stage's
+//    second half of MFMAs runs. A stage is two 16x16x128 FP4 MFMAs per tile
 //    pair; the lane that holds a row's 32-element block also hands the MFMA
 //    that block's E8M0 byte, so the scales are applied inside the matrix
 //    core and the epilogue has no per-row scale.
@@ -135,7 +137,7 @@ __device__ inline void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, void* lds_base
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE>
+template <int BM, int BN, int WGM, int WGN, int MODE, int NS>
 struct MxTile {
   static constexpr int kThreads = 64 * WGM * WGN;
   static constexpr int WM = BM / WGM, WN = BN / WGN;   // per-wave tile
@@ -149,7 +151,11 @@ struct MxTile {
   static constexpr int kScaleLoads = (kScaleDw + kThreads - 1) / kThreads;
   static constexpr int kEpiStride = BN * 2 + 16;       // BF16 staging row (GATE_UP)
   static constexpr int kEpi = MODE == kMxGateUp ? BM * kEpiStride : 0;
-  static constexpr int kLds = (2 * kStage > kEpi) ? 2 * kStage : kEpi;
+  static constexpr int kLds = (NS * kStage > kEpi) ? NS * kStage : kEpi;
+  // The down epilogue stages a wave row block's rows in JH parts, each no
+  // larger than the K loop's stages.
+  static constexpr int kJH = (MODE == kMxDownY && WM * BN * 4 > kLds) ? 2 : 1;
+  static_assert(NS == 1 || NS == 2, "one or two stages");
   static_assert(BN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "stage must split evenly over the threads");
   static_assert(kRowsPerPass % 8 == 0, "the loader's chunk swizzle needs 8-row passes");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
@@ -177,10 +183,10 @@ struct MxArgs {
   int N, K, tiles_n, tiles_m_max;
 };
 
-template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void mx_grouped(const MxArgs p) {
-  using C = MxTile<BM, BN, WGM, WGN, MODE>;
+  using C = MxTile<BM, BN, WGM, WGN, MODE, NS>;
   // One LDS object: the stages (or the epilogue's staging), then the row
   // tables. With a single object the compiler does not make the LDS reads
   // of a K step wait for the next step's direct-to-LDS loads.
@@ -323,8 +329,8 @@ void mx_grouped(const MxArgs p) {
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmem_all();
     __syncthreads();
-    if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
-    const uint8_t* st = smem + (kt & 1) * C::kStage;
+    if (NS == 2 && kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
+    const uint8_t* st = smem + (NS == 2 ? (kt & 1) * C::kStage : 0);
     const uint8_t* ss = st + C::kCodes;
     // Pass s of the stage takes chunk g + 4s of each row (elements
     // 128s + 32g .. +31, the row's block 8kt + 4s + g) and the row's scale
@@ -342,6 +348,27 @@ void mx_grouped(const MxArgs p) {
         xa[j] = v8i{c.x, c.y, c.z, c.w, c.x, c.y, c.z, c.w};
         sx[j] = (int)(*reinterpret_cast<const uint32_t*>(ss + row * 8 + 4 * s) >> (8 * g));
       }
+      if (NS == 1 && s == 1) {
+        // one stage: the last pass's operands in registers, then the next
+        // step's loads, which overlap this pass's MFMAs
+        v4i wc[C::SN];
+        int sw[C::SN];
+#pragma unroll
+        for (int i = 0; i < C::SN; ++i) {
+          const int row = wn * C::WN + i * 16 + r16;
+          wc[i] = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4 * s));
+          sw[i] = (int)(*reinterpret_cast<const uint32_t*>(ss + row * 8 + 4 * s) >> (8 * g));
+        }
+        lds_barrier();
+        if (kt + 1 < nk) issue(0, kt + 1);
+#pragma unroll
+        for (int i = 0; i < C::SN; ++i) {
+          const v8i wb = v8i{wc[i].x, wc[i].y, wc[i].z, wc[i].w, wc[i].x, wc[i].y, wc[i].z, wc[i].w};
+#pragma unroll
+          for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_mxfp4(wb, xa[j], acc[i][j], sw[i], sx[j]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < C::SN; ++i) {
         const int row = wn * C::WN + i * 16 + r16;
@@ -356,23 +383,28 @@ void mx_grouped(const MxArgs p) {
 
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
-  if (MODE == kMxDownY) {
-    // y = w * acc in float32, staged through LDS one wm's rows at a time and
+  if constexpr (MODE == kMxDownY) {
+    // y = w * acc in float32, staged through LDS one wm's rows (or half of
+    // them) at a time and
     // written as whole row pieces (BN * 4 contiguous bytes of each of
     // 256 / BN rows per store instruction), as in the FP8 down projection:
     // straight from the MFMA registers an instruction covers 16 rows x 64
     // bytes, which drains markedly slower. 16-byte chunks XOR-swizzled by row.
     constexpr int kChunks = BN / 4;
     constexpr int kRowsPerInst = 64 / kChunks;
-    static_assert(C::WM * BN * 4 <= 2 * C::kStage, "a wm's rows must fit in the stages");
+    constexpr int kJH = C::kJH, kPartRows = C::WM / kJH, kPartJ = C::SM / kJH;
+    static_assert(kPartRows * BN * 4 <= C::kLds && C::SM % kJH == 0, "a part of a wm's rows must fit in the LDS");
     static_assert(kChunks >= 16 && 64 % kChunks == 0, "row pieces must tile a wave");
-    for (int pass = 0; pass < WGM; ++pass) {
-      __syncthreads();  // the K-loop stages (pass 0) or the previous pass's rows are read
-      if (wm == pass) {
 #pragma unroll
-        for (int j = 0; j < C::SM; ++j) {
-          const int rl = j * 16 + r16;
-          const float w = row_w[wm * C::WM + rl];
+    for (int pass = 0; pass < WGM * kJH; ++pass) {
+      const int pw = pass / kJH, ph = pass % kJH;
+      __syncthreads();  // the K-loop stages (pass 0) or the previous pass's rows are read
+      if (wm == pw) {
+#pragma unroll
+        for (int jl = 0; jl < kPartJ; ++jl) {
+          const int j = ph * kPartJ + jl;
+          const int rl = jl * 16 + r16;
+          const float w = row_w[wm * C::WM + j * 16 + r16];
 #pragma unroll
           for (int i = 0; i < C::SN; ++i) {
             const int chunk = wn * (C::WN / 4) + i * 4 + g;
@@ -385,8 +417,8 @@ void mx_grouped(const MxArgs p) {
       __syncthreads();
       const int c = lane % kChunks;
       const int n = n0 + c * 4;
-      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < C::WM; rl += (C::kThreads / 64) * kRowsPerInst) {
-        const int ml = pass * C::WM + rl;
+      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < kPartRows; rl += (C::kThreads / 64) * kRowsPerInst) {
+        const int ml = pw * C::WM + ph * kPartRows + rl;
         const int slot = row_tok[ml];
         const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
         if (slot >= 0 && n < N)
@@ -490,23 +522,27 @@ __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, c
 
 // Tile shapes as for the FP8 experts: 256 x 256 tiles of 8 waves; 128 x 128
 // tiles of 2 x 2 waves when groups average fewer than 512 rows, and 64 x 128
-// tiles of 1 x 2 waves below 192 rows.
+// tiles of 1 x 2 waves below 192 rows. The 64 x 128 tiles take one LDS stage
+// (26 KB instead of 52 KB, four workgroups per CU instead of three; the
+// registers allow no more): 11-14% less time for a whole two-pass FFN at 128
+// and 192 experts, the same results bit for bit. For the 128 x 128 tiles one
+// stage gained nothing, and they keep two.
 constexpr int64_t kMxSmallGroupRows = 512, kMxTinyGroupRows = 192;
 
-template <int BM, int BN, int WGM, int WGN, int MODE, int OCC>
+template <int BM, int BN, int WGM, int WGN, int MODE, int OCC, int NS = 2>
 hipError_t run_mx(MxArgs a, int64_t max_rows, hipStream_t stream) {
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles_m_max = (int)((max_rows + BM - 1) / BM + a.G);  // every group adds at most one partial tile
   const int64_t blocks = (int64_t)a.tiles_m_max * a.tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((mx_grouped<BM, BN, WGM, WGN, MODE, OCC>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
+  hipLaunchKernelGGL((mx_grouped<BM, BN, WGM, WGN, MODE, OCC, NS>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
                      stream, a);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t run_mx_auto(const MxArgs& a, int64_t max_rows, int64_t avg_rows, hipStream_t stream) {
-  if (avg_rows < kMxTinyGroupRows) return run_mx<64, 128, 1, 2, MODE, 2>(a, max_rows, stream);
+  if (avg_rows < kMxTinyGroupRows) return run_mx<64, 128, 1, 2, MODE, 3, 1>(a, max_rows, stream);
   if (avg_rows < kMxSmallGroupRows) return run_mx<128, 128, 2, 2, MODE, 2>(a, max_rows, stream);
   return run_mx<256, 256, 2, 4, MODE, 2>(a, max_rows, stream);
 }
