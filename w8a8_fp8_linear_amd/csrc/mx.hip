@@ -343,10 +343,11 @@ void mx_grouped(const MxArgs p) {
       int sx[C::SM];
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) {
-        const int row = BN + wm * C::WM + j * 16 + r16;
-        const v4i c = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4 * s));
+        // rows 16 apart share (row & 7), so one swizzled base serves them all
+        const int row0x = BN + wm * C::WM + r16;
+        const v4i c = *reinterpret_cast<const v4i*>(st + stage_off(row0x, g + 4 * s) + j * 16 * 128);
         xa[j] = v8i{c.x, c.y, c.z, c.w, c.x, c.y, c.z, c.w};
-        sx[j] = (int)(*reinterpret_cast<const uint32_t*>(ss + row * 8 + 4 * s) >> (8 * g));
+        sx[j] = (int)(*reinterpret_cast<const uint32_t*>(ss + row0x * 8 + 4 * s + j * 16 * 8) >> (8 * g));
       }
       if (NS == 1 && s == 1) {
         // one stage: the last pass's operands in registers, then the next
@@ -355,12 +356,15 @@ void mx_grouped(const MxArgs p) {
         int sw[C::SN];
 #pragma unroll
         for (int i = 0; i < C::SN; ++i) {
-          const int row = wn * C::WN + i * 16 + r16;
-          wc[i] = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4 * s));
-          sw[i] = (int)(*reinterpret_cast<const uint32_t*>(ss + row * 8 + 4 * s) >> (8 * g));
+          const int row0w = wn * C::WN + r16;
+          wc[i] = *reinterpret_cast<const v4i*>(st + stage_off(row0w, g + 4 * s) + i * 16 * 128);
+          sw[i] = (int)(*reinterpret_cast<const uint32_t*>(ss + row0w * 8 + 4 * s + i * 16 * 8) >> (8 * g));
         }
         lds_barrier();
-        if (kt + 1 < nk) issue(0, kt + 1);
+        // unconditional, so that the loop body stays one block and the first
+        // pass's MFMAs stay ahead of this pass's reads; past the last step
+        // every load is out of range and only zero-fills the stage
+        issue(0, kt + 1);
 #pragma unroll
         for (int i = 0; i < C::SN; ++i) {
           const v8i wb = v8i{wc[i].x, wc[i].y, wc[i].z, wc[i].w, wc[i].x, wc[i].y, wc[i].z, wc[i].w};
@@ -371,16 +375,29 @@ void mx_grouped(const MxArgs p) {
       }
 #pragma unroll
       for (int i = 0; i < C::SN; ++i) {
-        const int row = wn * C::WN + i * 16 + r16;
-        const v4i c = *reinterpret_cast<const v4i*>(st + stage_off(row, g + 4 * s));
+        const int row0w = wn * C::WN + r16;
+        const v4i c = *reinterpret_cast<const v4i*>(st + stage_off(row0w, g + 4 * s) + i * 16 * 128);
         const v8i wb = v8i{c.x, c.y, c.z, c.w, c.x, c.y, c.z, c.w};
-        const int sw = (int)(*reinterpret_cast<const uint32_t*>(ss + row * 8 + 4 * s) >> (8 * g));
+        const int sw = (int)(*reinterpret_cast<const uint32_t*>(ss + row0w * 8 + 4 * s + i * 16 * 8) >> (8 * g));
 #pragma unroll
         for (int j = 0; j < C::SM; ++j) acc[i][j] = mfma_16x16x128_mxfp4(wb, xa[j], acc[i][j], sw, sx[j]);
+      }
+      if (NS == 1) {
+        // pin the first pass's MFMAs here: otherwise they are sunk below the
+        // next step's loads, and both passes' operands are live together
+#pragma unroll
+        for (int i = 0; i < C::SN; ++i)
+#pragma unroll
+          for (int j = 0; j < C::SM; ++j) asm volatile("" ::"a"(acc[i][j]));
       }
     }
   }
 
+  if (NS == 1) {
+    // the last step's zero-fill loads land before the epilogue reuses the LDS
+    wait_vmem_all();
+    __syncthreads();
+  }
   // acc[i][j][r]: tile row wm * WM + 16 j + lane % 16, stage (weight) row
   // wn * WN + 16 i + 4 (lane / 16) + r.
   if constexpr (MODE == kMxDownY) {
@@ -523,10 +540,10 @@ __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, c
 // Tile shapes as for the FP8 experts: 256 x 256 tiles of 8 waves; 128 x 128
 // tiles of 2 x 2 waves when groups average fewer than 512 rows, and 64 x 128
 // tiles of 1 x 2 waves below 192 rows. The 64 x 128 tiles take one LDS stage
-// (26 KB instead of 52 KB, four workgroups per CU instead of three; the
-// registers allow no more): 11-14% less time for a whole two-pass FFN at 128
-// and 192 experts, the same results bit for bit. For the 128 x 128 tiles one
-// stage gained nothing, and they keep two.
+// (26 KB instead of 52 KB) at three waves per SIMD (78-82 VGPRs), so six
+// workgroups fit on a CU instead of three: 16-19% less time for a whole
+// two-pass FFN at 128 and 192 experts, the same results bit for bit. For the
+// 128 x 128 tiles one stage gained nothing, and they keep two.
 constexpr int64_t kMxSmallGroupRows = 512, kMxTinyGroupRows = 192;
 
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC, int NS = 2>
