@@ -172,6 +172,15 @@ __device__ inline void store16_nt(void* p, float4 v) {
 
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// At most N vector memory operations of this wave outstanding (vmcnt(N));
+// the other counters are not waited for.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  constexpr int kImm = (N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14);
+  __builtin_amdgcn_s_waitcnt(kImm);
+}
+
 // A workgroup barrier that orders LDS only: this wave's LDS accesses are
 // complete, then all waves meet. Unlike __syncthreads() it does not wait for
 // the wave's outstanding global loads and stores (on this GPU one counter

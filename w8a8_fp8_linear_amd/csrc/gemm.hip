@@ -194,11 +194,18 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
 // tiles. Every workgroup reads all M input rows (from L2), so for M > 16 two
 // weight tiles per workgroup halve that traffic; a wave's input fragments
 // serve both tiles. Each output's sum runs in the same order for any NT.
-template <int MT, int U, int NT = 1>
+// XL = the input rows go global -> LDS as whole 128-byte row pieces (one
+// load instruction per 8 rows and K step) instead of straight into the MFMA
+// layout (16 rows x 64 bytes per instruction); the sums are the same.
+template <int MT, int U, int NT = 1, bool XL = false>
 __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A, const float* __restrict__ sa,
                                                    const uint8_t* __restrict__ W, const float* __restrict__ sw,
                                                    uint16_t* __restrict__ Y, int M, int N, int K) {
   __shared__ v4f red[3][NT][MT][64];
+  // XL: each wave's input rows for its U steps, [U][16 MT rows][128 bytes],
+  // the 16-byte pieces of a row swizzled by (row & 7)
+  constexpr int kXRows = 16 * MT;
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[XL ? 4 : 1][XL ? U : 1][XL ? kXRows * 128 : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16 * NT;
@@ -227,8 +234,32 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (K + 127) >> 7;
+  const int xr8 = lane >> 3, xslot = lane & 7;
   for (int kt = wave; kt < nk; kt += 4 * U) {
     v8i wf[U][NT], xf[U][MT];
+    if constexpr (XL) {
+      // The input rows first, as whole 128-byte row pieces into this wave's
+      // LDS slice: instruction (u, q) takes rows 8q .. 8q + 7 of step u, lane
+      // l row 8q + l / 8 and the piece (l % 8) ^ (row % 8), which lands in
+      // slot l % 8 of the row. Rows at or past M are not loaded: their MFMA
+      // columns are never stored.
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k0 = (kt + 4 * u) << 7;
+        const bool live = kt + 4 * u < nk;
+#pragma unroll
+        for (int q = 0; q < 2 * MT; ++q) {
+          if (8 * q < M) {
+            const int row = 8 * q + xr8;
+            const int piece = xslot ^ (row & 7);
+            const int c = k0 + 16 * piece;
+            const uint32_t off =
+                (live && row < M && c < K) ? (uint32_t)row * (uint32_t)K + (uint32_t)c : kOutOfRange;
+            buffer_load16_lds(rA, &xs[wave][u][8 * q * 128], off);
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k0 = (kt + 4 * u) << 7;
@@ -243,13 +274,29 @@ __global__ __launch_bounds__(256) void gemm_skinny(const uint8_t* __restrict__ A
         const v4i hi = buffer_load16(rW, o1 == kOutOfRange ? o1 : wrow + o1);
         wf[u][i] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
+      if constexpr (!XL) {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const uint32_t xrow = (uint32_t)(t * 16 + r16) * (uint32_t)K;
-        const v4i xl = buffer_load16(rA, o0 == kOutOfRange ? o0 : xrow + o0);
-        const v4i xh = buffer_load16(rA, o1 == kOutOfRange ? o1 : xrow + o1);
-        xf[u][t] = v8i{xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+        for (int t = 0; t < MT; ++t) {
+          const uint32_t xrow = (uint32_t)(t * 16 + r16) * (uint32_t)K;
+          const v4i xl = buffer_load16(rA, o0 == kOutOfRange ? o0 : xrow + o0);
+          const v4i xh = buffer_load16(rA, o1 == kOutOfRange ? o1 : xrow + o1);
+          xf[u][t] = v8i{xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+        }
       }
+    }
+    if constexpr (XL) {
+      // the input pieces have landed once only the weight loads are outstanding
+      wait_vmcnt<2 * U * NT>();
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int row = t * 16 + r16;
+          const uint8_t* xrow = &xs[wave][u][row * 128];
+          const v4i xl = *reinterpret_cast<const v4i*>(xrow + ((g ^ (row & 7)) << 4));
+          const v4i xh = *reinterpret_cast<const v4i*>(xrow + (((g + 4) ^ (row & 7)) << 4));
+          xf[u][t] = v8i{xl.x, xl.y, xl.z, xl.w, xh.x, xh.y, xh.z, xh.w};
+        }
     }
     // keep every load of this round ahead of the first MFMA: bytes in flight
     // are what this kernel is limited by
@@ -458,8 +505,11 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
                        y, (int)M, (int)N, (int)K);
     return hipGetLastError();
   }
+  // 17 to 32 rows: the input rows go through LDS as whole 128-byte row
+  // pieces (7.2 -> 6.6 us for 32 rows of the 8192 x 2048 layer; at 8 to 16
+  // rows the extra LDS hop costs as much as it saves)
   if (M <= 32) {
-    hipLaunchKernelGGL((gemm_skinny<2, 4, 2>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, stream, a, sa, w, sw,
+    hipLaunchKernelGGL((gemm_skinny<2, 4, 2, true>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, stream, a, sa, w, sw,
                        y, (int)M, (int)N, (int)K);
     return hipGetLastError();
   }
