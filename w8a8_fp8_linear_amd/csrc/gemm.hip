@@ -20,10 +20,11 @@
 //    so that each of the 8 XCDs walks a compact block of tiles (its own L2).
 //  * gemm_skinny: at most 32 tokens (decode). The time is the weight stream:
 //    the pages note that single-stream generation is limited by weight
-//    bandwidth rather than arithmetic ("What --fast-math does"). A workgroup owns 16 weight rows, its 4 waves
-//    split K, each lane loads its MFMA operands straight from global memory
-//    with 16-byte loads (every weight byte is read once), and the partial
-//    sums meet in LDS.
+//    bandwidth rather than arithmetic ("What --fast-math does"). A workgroup
+//    owns 16 or 32 weight rows, its 4 waves split K, each lane loads its
+//    weight operands straight from global memory with 16-byte loads (every
+//    weight byte is read once), and the partial sums meet in LDS. The input
+//    rows are loaded the same way, or at 17 to 32 rows staged through LDS.
 //  * gemm_skinny_q: gemm_skinny with the per-token quantisation of its BF16
 //    input fused in (one launch instead of two). For K <= 2048 one round of
 //    the skinny loop covers all of K, so the 4 waves of a workgroup load

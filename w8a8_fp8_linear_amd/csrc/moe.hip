@@ -23,8 +23,9 @@
 //    No host synchronisation: every later kernel reads the offsets from
 //    device memory and derives its own tile from them.
 //  * grouped_tiled: the dense tiled pipeline (WGM x WGN waves, 128-deep K
-//    steps staged global -> LDS by direct buffer loads, double-buffered,
-//    16x16x128 E4M3 MFMAs) over sorted slots, one expert per m-tile:
+//    steps staged global -> LDS by direct buffer loads, double-buffered for
+//    the large tiles and in one stage for the small ones, 16x16x128 E4M3
+//    MFMAs) over sorted slots, one expert per m-tile:
 //      GATE_UP    A rows gathered through the permutation (slot -> token),
 //                 BF16 gate/up output in sorted order;
 //      GATE_UP_H  the same product with gate and up weight blocks
@@ -41,9 +42,10 @@
 //  * combine_slots: out[t] = bf16(sum_j y[t*k + j]) over valid slots
 //    (float32 rows and sums, one rounding), added in the fixed order
 //    j = 0, 1, ... (deterministic, no atomics; float32 atomics measured ~3x
-//    slower than this whole stage). The k rows of a token are contiguous, so
-//    this is one streaming pass. combine_quant also quantises each output row
-//    per token (the next pass's input) in the same pass.
+//    slower than this whole stage). The k rows of a token are contiguous in
+//    the per-stage layout and gathered through the slot -> row map in the
+//    full pass; either way one streaming pass. combine_quant also quantises
+//    each output row per token (the next pass's input) in the same pass.
 #include <algorithm>
 
 #include "device.h"
