@@ -82,6 +82,48 @@ __device__ inline void sum_slots8(const float* __restrict__ y, const int32_t* __
   }
 }
 
+// Columns of thread r (0 <= r < H / 8) of a row: two runs of 4, ca .. ca + 3
+// and cb .. cb + 3. The 64 threads of a 512-column block take the block's
+// first half as 4-column runs in lane order and the second half likewise, so
+// each of a wave's 16-byte load instructions reads 1 KB contiguous. A last,
+// shorter block of W columns is split at W / 2 (H is a multiple of 8).
+__device__ inline void split_cols8(int r, int H, int& ca, int& cb) {
+  const int base = (r >> 6) << 9, l = r & 63;
+  const int w = min(512, H - base);
+  ca = base + 4 * l;
+  cb = base + (w >> 1) + 4 * l;
+}
+
+// sum_slots8 over the columns ca .. ca + 3 (a) and cb .. cb + 3 (b).
+__device__ inline void sum_slots_split(const float* __restrict__ y, const int32_t* __restrict__ ids,
+                                       const int32_t* __restrict__ slot_row, int64_t t, int topk, int Eids, int H,
+                                       int ca, int cb, float4& a, float4& b) {
+  a = make_float4(0.f, 0.f, 0.f, 0.f);
+  b = a;
+  constexpr int kBatch = 8;
+  for (int j0 = 0; j0 < topk; j0 += kBatch) {
+    v4f u[kBatch], v[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int j = j0 + jj;
+      const int64_t slot = t * topk + (j < topk ? j : 0);
+      const int id = ids[slot];
+      ok[jj] = j < topk && id >= 0 && id < Eids;
+      const int64_t row = !ok[jj] ? 0 : slot_row ? (int64_t)slot_row[slot] : slot;
+      const float* src = y + row * H;
+      u[jj] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + ca));
+      v[jj] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + cb));
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      if (!ok[jj]) continue;
+      a.x += u[jj][0]; a.y += u[jj][1]; a.z += u[jj][2]; a.w += u[jj][3];
+      b.x += v[jj][0]; b.y += v[jj][1]; b.z += v[jj][2]; b.w += v[jj][3];
+    }
+  }
+}
+
 __device__ inline uint4 to_bf16x8(float4 a, float4 b) {
   return make_uint4(bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y), bf16x2_rne(b.z, b.w));
 }

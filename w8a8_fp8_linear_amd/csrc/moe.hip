@@ -621,10 +621,13 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
   const int per_row = H >> 3;
   const int64_t t = i / per_row;
   if (t >= T) return;
-  const int c0 = (int)(i - t * per_row) << 3;
+  int ca, cb;
+  split_cols8((int)(i - t * per_row), H, ca, cb);
   float4 a, b;
-  sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
-  *reinterpret_cast<uint4*>(out + t * H + c0) = to_bf16x8(a, b);
+  sum_slots_split(y, ids, slot_row, t, topk, Eids, H, ca, cb, a, b);
+  const uint4 o = to_bf16x8(a, b);
+  *reinterpret_cast<uint2*>(out + t * H + ca) = make_uint2(o.x, o.y);
+  *reinterpret_cast<uint2*>(out + t * H + cb) = make_uint2(o.z, o.w);
 }
 
 // The combine with the next pass's per-token quantisation fused in: one
@@ -643,13 +646,16 @@ __global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y
   uint32_t amax = 0;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int c0 = (tid + 256 * p) << 3;
+    const int r8 = tid + 256 * p;
     vb[p] = make_uint4(0u, 0u, 0u, 0u);
-    if (c0 < H) {
+    if ((r8 << 3) < H) {
+      int ca, cb;
+      split_cols8(r8, H, ca, cb);
       float4 a, b;
-      sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
+      sum_slots_split(y, ids, slot_row, t, topk, Eids, H, ca, cb, a, b);
       vb[p] = to_bf16x8(a, b);
-      *reinterpret_cast<uint4*>(out + t * H + c0) = vb[p];
+      *reinterpret_cast<uint2*>(out + t * H + ca) = make_uint2(vb[p].x, vb[p].y);
+      *reinterpret_cast<uint2*>(out + t * H + cb) = make_uint2(vb[p].z, vb[p].w);
       const uint32_t m = absmax8(vb[p]);
       amax = amax > m ? amax : m;
     }
@@ -662,8 +668,14 @@ __global__ __launch_bounds__(256) void combine_quant(const float* __restrict__ y
   const float r = 1.0f / s;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int c0 = (tid + 256 * p) << 3;
-    if (c0 < H) *reinterpret_cast<uint2*>(q + t * H + c0) = quant8(vb[p], s, r);
+    const int r8 = tid + 256 * p;
+    if ((r8 << 3) < H) {
+      int ca, cb;
+      split_cols8(r8, H, ca, cb);
+      const uint2 c = quant8(vb[p], s, r);
+      *reinterpret_cast<uint32_t*>(q + t * H + ca) = c.x;
+      *reinterpret_cast<uint32_t*>(q + t * H + cb) = c.y;
+    }
   }
   if (tid == 0) qs[t] = s;
 }

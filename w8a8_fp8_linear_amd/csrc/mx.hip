@@ -515,7 +515,8 @@ void mx_grouped(const MxArgs p) {
 // out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots,
 // in the order j = 0, 1, ...; with QUANT also the MXFP4 codes and scales of
 // the BF16 row (exactly what mx_quant_bf16 makes of it). One thread per 8
-// columns; H % 32 == 0, so a block's four threads form an aligned quad.
+// columns; with QUANT they are consecutive (H % 32 == 0, so a block's four
+// threads form an aligned quad), without it two runs of 4 (split_cols8).
 template <bool QUANT>
 __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, const int32_t* __restrict__ ids,
                                                   const int32_t* __restrict__ slot_row, int64_t T, int topk, int Eids,
@@ -525,15 +526,25 @@ __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, c
   const int per_row = H >> 3;
   const int64_t t = i / per_row;
   if (t >= T) return;
-  const int c0 = (int)(i - t * per_row) << 3;
   float4 a, b;
-  sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
-  const uint4 v = to_bf16x8(a, b);
-  *reinterpret_cast<uint4*>(out + t * H + c0) = v;
-  if (QUANT) {
+  if constexpr (QUANT) {
+    // 8 consecutive columns per thread: a quad of threads holds one block
+    const int c0 = (int)(i - t * per_row) << 3;
+    sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
+    const uint4 v = to_bf16x8(a, b);
+    *reinterpret_cast<uint4*>(out + t * H + c0) = v;
     uint32_t code;
     reinterpret_cast<uint32_t*>(q)[i] = mx_quad_quant(v, &code);
     if ((i & 3) == 0) s[i >> 2] = (uint8_t)code;
+  } else {
+    // two runs of 4 columns per thread, so that every load instruction
+    // reads 1 KB contiguous (the same sums)
+    int ca, cb;
+    split_cols8((int)(i - t * per_row), H, ca, cb);
+    sum_slots_split(y, ids, slot_row, t, topk, Eids, H, ca, cb, a, b);
+    const uint4 v = to_bf16x8(a, b);
+    *reinterpret_cast<uint2*>(out + t * H + ca) = make_uint2(v.x, v.y);
+    *reinterpret_cast<uint2*>(out + t * H + cb) = make_uint2(v.z, v.w);
   }
 }
 
