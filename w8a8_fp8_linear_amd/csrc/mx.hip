@@ -111,6 +111,20 @@ __device__ inline uint32_t mx_quad_quant(uint4 v, uint32_t* code) {
   return e2m1_pack<8>(x, mx_inv_scale(c));
 }
 
+// The same for 4 BF16 values per lane (w0, w1) held by an aligned group of 8
+// lanes (lane p of it elements 4p .. 4p+3 of the block). Returns the lane's 2
+// code bytes; *code gets the block's E8M0 byte.
+__device__ inline uint32_t mx_oct_quant(uint32_t w0, uint32_t w1, uint32_t* code) {
+  uint32_t m = max(max(w0 & 0x7FFFu, (w0 >> 16) & 0x7FFFu), max(w1 & 0x7FFFu, (w1 >> 16) & 0x7FFFu));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
+  const uint32_t c = mx_scale_code(m << 16);
+  const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  *code = c;
+  return e2m1_pack<4>(x, mx_inv_scale(c));
+}
+
 // One thread per 8 values; chunks = M * K / 8 with K % 32 == 0, so the four
 // threads of a block are an aligned quad of one row and leave together.
 __global__ __launch_bounds__(256) void mx_quant_bf16(const uint16_t* __restrict__ x, int64_t chunks,
@@ -515,9 +529,13 @@ void mx_grouped(const MxArgs p) {
 // out[t, c] = bf16( sum_j y[t * topk + j, c] ) over the token's valid slots,
 // in the order j = 0, 1, ...; with QUANT also the MXFP4 codes and scales of
 // the BF16 row (exactly what mx_quant_bf16 makes of it). One thread per 8
-// columns; with QUANT they are consecutive (H % 32 == 0, so a block's four
-// threads form an aligned quad), without it two runs of 4 (split_cols8).
-template <bool QUANT>
+// columns: two runs of 4 (split_cols8) if SPLIT, so that every load
+// instruction reads 1 KB contiguous. Otherwise 8 consecutive columns, and
+// with H % 32 == 0 a block's four threads form an aligned quad. With SPLIT
+// and QUANT H % 64 == 0: both halves of every 512-column block (or of the
+// row's shorter last block) are whole 32-column blocks, each held by an
+// aligned group of 8 threads, 4 columns each.
+template <bool QUANT, bool SPLIT>
 __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, const int32_t* __restrict__ ids,
                                                   const int32_t* __restrict__ slot_row, int64_t T, int topk, int Eids,
                                                   int H, uint16_t* __restrict__ out,
@@ -527,24 +545,36 @@ __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, c
   const int64_t t = i / per_row;
   if (t >= T) return;
   float4 a, b;
-  if constexpr (QUANT) {
-    // 8 consecutive columns per thread: a quad of threads holds one block
-    const int c0 = (int)(i - t * per_row) << 3;
-    sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
-    const uint4 v = to_bf16x8(a, b);
-    *reinterpret_cast<uint4*>(out + t * H + c0) = v;
-    uint32_t code;
-    reinterpret_cast<uint32_t*>(q)[i] = mx_quad_quant(v, &code);
-    if ((i & 3) == 0) s[i >> 2] = (uint8_t)code;
-  } else {
-    // two runs of 4 columns per thread, so that every load instruction
-    // reads 1 KB contiguous (the same sums)
+  if constexpr (SPLIT) {
     int ca, cb;
     split_cols8((int)(i - t * per_row), H, ca, cb);
     sum_slots_split(y, ids, slot_row, t, topk, Eids, H, ca, cb, a, b);
     const uint4 v = to_bf16x8(a, b);
     *reinterpret_cast<uint2*>(out + t * H + ca) = make_uint2(v.x, v.y);
     *reinterpret_cast<uint2*>(out + t * H + cb) = make_uint2(v.z, v.w);
+    if constexpr (QUANT) {
+      uint32_t code_a, code_b;
+      const uint32_t qa = mx_oct_quant(v.x, v.y, &code_a);
+      const uint32_t qb = mx_oct_quant(v.z, v.w, &code_b);
+      uint8_t* qrow = q + t * (H / 2);
+      *reinterpret_cast<uint16_t*>(qrow + ca / 2) = (uint16_t)qa;
+      *reinterpret_cast<uint16_t*>(qrow + cb / 2) = (uint16_t)qb;
+      if ((i & 7) == 0) {
+        s[t * (H / 32) + ca / 32] = (uint8_t)code_a;
+        s[t * (H / 32) + cb / 32] = (uint8_t)code_b;
+      }
+    }
+  } else {
+    // 8 consecutive columns per thread: a quad of threads holds one block
+    const int c0 = (int)(i - t * per_row) << 3;
+    sum_slots8(y, ids, slot_row, t, topk, Eids, H, c0, a, b);
+    const uint4 v = to_bf16x8(a, b);
+    *reinterpret_cast<uint4*>(out + t * H + c0) = v;
+    if constexpr (QUANT) {
+      uint32_t code;
+      reinterpret_cast<uint32_t*>(q)[i] = mx_quad_quant(v, &code);
+      if ((i & 3) == 0) s[i >> 2] = (uint8_t)code;
+    }
   }
 }
 
@@ -647,12 +677,15 @@ hipError_t launch_mx_down_combine(const uint8_t* qh, const uint8_t* sh, const in
   if (err != hipSuccess) return err;
   const int64_t threads = T * (H / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
-  if (out_q != nullptr)
-    hipLaunchKernelGGL(combine_mx<true>, grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E, (int)H,
-                       out, out_q, out_s);
+  if (out_q != nullptr && H % 64 == 0)
+    hipLaunchKernelGGL((combine_mx<true, true>), grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E,
+                       (int)H, out, out_q, out_s);
+  else if (out_q != nullptr)
+    hipLaunchKernelGGL((combine_mx<true, false>), grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E,
+                       (int)H, out, out_q, out_s);
   else
-    hipLaunchKernelGGL(combine_mx<false>, grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E, (int)H,
-                       out, nullptr, nullptr);
+    hipLaunchKernelGGL((combine_mx<false, true>), grid, dim3(256), 0, stream, y, ids, slot_row, T, (int)topk, (int)E,
+                       (int)H, out, nullptr, nullptr);
   return hipGetLastError();
 }
 
