@@ -23,7 +23,7 @@
 //  * mx_grouped: the grouped expert pipeline with 256-deep K steps: per row
 //    and stage, 128 bytes of codes (staged and swizzled as in the FP8
 //    kernel) and the row's 8 scale bytes, both by direct buffer -> LDS
-//    loads, double-buffered (NS = 2) or, for the smallest tiles, in one
+//    loads, double-buffered (NS = 2) or, for the small tiles, in one
 //    stage (NS = 1) that the next step's loads refill while the stage's
 //    second half of MFMAs runs. A stage is two 16x16x128 FP4 MFMAs per tile
 //    pair; the lane that holds a row's 32-element block also hands the MFMA
