@@ -115,14 +115,29 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
     # back-to-back steps (61-67 us per GEMM against 53-56 us before and
     # after), then holds a steady clock. The step runs back to back for
     # settle_ms first so that the warm-up and the timed steps see that
-    # steady state, as a server running prefill continuously does.
+    # steady state, as a server running prefill continuously does. The first
+    # kClockSteps settle steps also time their GEMM and read the shader clock
+    # right after it (clock_probe, 4 us per step), which shows the throttle.
+    kClockSteps = 400
+    clk = torch.empty((kClockSteps, 256, 2), dtype=torch.int64, device="cuda")
+    clk_evs = _events(kClockSteps)
     settled = 0
     t_end = time.perf_counter() + settle_ms * 1e-3
-    while time.perf_counter() < t_end:
+    while time.perf_counter() < t_end or settled < kClockSteps:
         for _ in range(10):
-            step()
-        settled += 10
+            if settled < kClockSteps:
+                a, b = clk_evs[settled]
+                w8.quantize_per_token(x, xq, xs)
+                a.record(stream)
+                w8.w8a8_gemm(xq, xs, wq, ws, out=y)
+                b.record(stream)
+                w8.clock_probe(256, clk[settled])
+            else:
+                step()
+            settled += 1
         torch.cuda.synchronize()
+    # (the clock readings are summarised after the timed section: host work
+    # here would leave the GPU idle and let the clock controller reset)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -199,6 +214,12 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
 
     torch.cuda.synchronize()
     y_bits = y.view(torch.int16).cpu().numpy().view(np.uint16)  # compared with the oracle's in cpu_baselines
+    clk_cpu = clk.cpu()
+    clock = []
+    for lo, hi in ((0, 25), (25, 100), (100, 200), (200, 400)):
+        clock.append({"launches": [lo, hi - 1],
+                      "gemm_us_avg": round(1e3 * sum(a.elapsed_time(b) for a, b in clk_evs[lo:hi]) / (hi - lo), 2),
+                      "clock_ghz_avg": round(sum(w8.clock_ghz(clk_cpu[i]) for i in range(lo, hi)) / (hi - lo), 3)})
     flops = 2.0 * M * N * K
     gemm_bytes = M * K + N * K + 2 * M * N + 4 * (M + N)
     q_bytes = 2 * M * K + M * K + 4 * M
@@ -211,6 +232,7 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
         "gemm_ms_avg": gemm_avg, "gemm_ms_min": gemm_timed_ms[0], "gemm_ms_max": gemm_timed_ms[-1],
         "gemm_ms_median": gemm_timed_ms[len(gemm_timed_ms) // 2], "gemm_launches_timed": len(gemm_timed_ms),
         "gemm_ms_back_to_back": gemm_b2b_avg, "settle_ms": settle_ms, "settle_steps": settled,
+        "settle_clock": clock,
         "gemm_tflops": flops / (gemm_avg * 1e-3) / 1e12, "gemm_flops": flops, "gemm_bytes": gemm_bytes,
         "quant_ms_avg": q_avg, "quant_gbs": q_bytes / (q_avg * 1e-3) / 1e9, "quant_bytes": q_bytes,
         "tokens_per_s": M * steps / wall, "y_bits": y_bits,
@@ -931,7 +953,11 @@ def main():
                                    round(pre["gemm_ms_max"] * 1e3, 3)],
         "gemm_us_back_to_back_launches": round(pre["gemm_ms_back_to_back"] * 1e3, 3),
         "settle": {"ms": pre["settle_ms"], "steps": pre["settle_steps"],
-                   "what": "untimed back-to-back steps before the warm-up steps (power-controller transient)"},
+                   "what": "untimed back-to-back steps before the warm-up steps (power-controller transient)",
+                   "clock_by_launch": pre["settle_clock"],
+                   "clock_what": "the first 400 settle steps: each GEMM timed with HIP events, then clock_probe "
+                                 "(shader cycles over 4 us of the 100 MHz clock, median of 256 one-wave "
+                                 "workgroups) read right after it on the same stream"},
         "quant_us_avg": round(pre["quant_ms_avg"] * 1e3, 3),
         "quant_GBs": round(pre["quant_gbs"], 1),
         "tokens_per_s": round(pre["tokens_per_s"], 1),

@@ -152,6 +152,25 @@ int64_t read_probe_sink_words(int64_t bytes);
 int read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
+ * clock_probe — the shader clock, for measurement.
+ *
+ * The pages compare the fast-math path's throughput with the default maths
+ * (Lernex/Metis-1.6-Logos-FP8, "What --fast-math does"); on this GPU the
+ * throughput of a steady load depends on the clock the power controller
+ * sets, which this call reads. It launches n workgroups of one wave; lane 0
+ * of workgroup b spins until the constant 100 MHz clock has advanced by 400
+ * ticks (4 us) and writes the shader cycles counted over the same span to
+ * out[2 b] and the constant-clock ticks to out[2 b + 1], so
+ * 0.1 * out[2 b] / out[2 b + 1] is the shader clock in GHz. Enqueued right
+ * after a kernel on the same stream, it shows the clock that kernel ran at
+ * as far as the power controller's setting goes.
+ *   out  [2 n] uint64 output, 16-byte aligned
+ *   n    number of workgroups, 0 .. 65536
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, MISALIGNED, DEVICE, LAUNCH.
+ */
+int clock_probe(uint64_t* out, int64_t n, hipStream_t stream);
+
+/*
  * w8a16_gemm — the default maths: BF16 activations times the E4M3 weights
  * widened to BF16, on the BF16 matrix units.
  *

@@ -195,6 +195,16 @@ def test_fp8_linear_noalloc_argument_errors():
     assert f(P, P, P, P + 8, 64, 16, 16, 1, None) == MIS
 
 
+def test_clock_probe_argument_errors():
+    f = w8.lib().clock_probe
+    assert f(P, -1, None) == SHAPE
+    assert f(P, 65537, None) == UNSUP
+    assert f(P, 0, None) == OK
+    assert f(None, 4, None) == NULL
+    assert f(P + 8, 4, None) == MIS
+    assert f(P, 4, None) == DEV
+
+
 def test_read_probe_argument_errors():
     f = w8.lib().read_probe
     assert w8.lib().read_probe_sink_words(16809984) == 513

@@ -109,3 +109,17 @@ def test_read_probe_checksums(nbytes):
     padded[:nbytes] = data
     want = np.bitwise_xor.reduce(padded.view(np.uint32).reshape(-1, 8192), axis=1)
     assert np.array_equal(sink[:want.size], want)
+
+
+def test_clock_probe_reads_a_plausible_clock():
+    """clock_probe: every workgroup spans at least 400 ticks of the 100 MHz clock, and the shader
+    clock it reports lies between 0.5 and 3 GHz (the chip's top clock is 2.4 GHz)."""
+    print("[clock_probe] 256 workgroups", flush=True)
+    out = w8.clock_probe(256)
+    torch.cuda.synchronize()
+    v = out.cpu().numpy()
+    assert (v[:, 1] >= 400).all() and (v[:, 1] < 100000).all(), v[:, 1].min()
+    ghz = 0.1 * v[:, 0] / v[:, 1]
+    assert (ghz > 0.5).all() and (ghz < 3.0).all(), (ghz.min(), ghz.max())
+    assert abs(w8.clock_ghz(out) - float(np.median(ghz))) < 1e-9
+    print("clock_probe median GHz", float(np.median(ghz)), flush=True)

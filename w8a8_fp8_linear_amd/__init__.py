@@ -53,6 +53,7 @@ _SIGNATURES = {
     "e4m3_from_f32": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "read_probe_sink_words": (ctypes.c_int64, [_c_i64]),
     "read_probe": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "clock_probe": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr]),
     "bf16_from_f32": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "moe_down_combine": (ctypes.c_int, [_c_ptr] * 10 + [_c_i64] * 5 + [ctypes.c_int, _c_ptr]),
     "w8a8_grouped_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
@@ -305,6 +306,29 @@ def bf16_from_f32(v):
     y = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
     _check("bf16_from_f32", lib().bf16_from_f32(v.data_ptr(), v.numel(), y.data_ptr(), _stream(v)))
     return y
+
+
+def clock_probe(n=256, out=None, device="cuda"):
+    """Enqueue the shader-clock probe (n one-wave workgroups) on the current
+    stream. Returns out, int64 [n, 2]: shader cycles and 100 MHz ticks per
+    workgroup over the same span (about 4 us)."""
+    import torch
+
+    if out is None:
+        out = torch.empty((n, 2), dtype=torch.int64, device=device)
+    if out.dtype != torch.int64 or not out.is_cuda or not out.is_contiguous() or out.numel() < 2 * n:
+        raise ValueError("out must be a contiguous int64 GPU tensor with at least 2 * n entries")
+    _check("clock_probe", lib().clock_probe(out.data_ptr(), n, _stream(out)))
+    return out
+
+
+def clock_ghz(out):
+    """Median shader clock in GHz over the workgroups of a clock_probe result
+    (a CPU or GPU int64 [n, 2] tensor)."""
+    import torch
+
+    v = out.detach().to("cpu", torch.float64).view(-1, 2)
+    return float(torch.median(0.1 * v[:, 0] / v[:, 1]))
 
 
 def read_probe(t, sink=None):

@@ -163,6 +163,17 @@ int read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stre
   return launch_status(w8a8::launch_read_probe(p, bytes, sink, stream));
 }
 
+int clock_probe(uint64_t* out, int64_t n, hipStream_t stream) {
+  if (n < 0) return W8A8_ERR_BAD_SHAPE;
+  if (n > 65536) return W8A8_ERR_UNSUPPORTED;
+  if (n == 0) return W8A8_OK;
+  if (!out) return W8A8_ERR_NULL_ARG;
+  if (!aligned16(out)) return W8A8_ERR_MISALIGNED;
+  const int d = check_device();
+  if (d != W8A8_OK) return d;
+  return launch_status(w8a8::launch_clock_probe(out, n, stream));
+}
+
 size_t fp8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0 || !mul_ok(M, K)) return 0;
   return (size_t)(align256(M * K) + align256(M * 4));

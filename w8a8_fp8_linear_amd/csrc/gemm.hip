@@ -478,6 +478,24 @@ __global__ __launch_bounds__(256) void read_probe(const uint8_t* __restrict__ p,
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// The shader clock: lane 0 of each one-wave workgroup spins until the
+// constant 100 MHz clock has advanced by kClockProbeTicks and counts the
+// shader cycles (s_memtime) over the same span.
+constexpr unsigned long long kClockProbeTicks = 400;  // 4 us
+
+__global__ __launch_bounds__(64) void clock_probe(uint64_t* __restrict__ out) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long r1;
+  do {
+    r1 = __builtin_amdgcn_s_memrealtime();
+  } while (r1 - r0 < kClockProbeTicks);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  out[2 * blockIdx.x] = (uint64_t)(t1 - t0);
+  out[2 * blockIdx.x + 1] = (uint64_t)(r1 - r0);
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t run_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -521,6 +539,12 @@ hipError_t launch_read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hi
   if (bytes == 0) return hipSuccess;
   hipLaunchKernelGGL(read_probe, dim3((unsigned)((bytes + kProbeBytesPerBlock - 1) / kProbeBytesPerBlock)), dim3(256),
                      0, stream, p, bytes, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_clock_probe(uint64_t* out, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(clock_probe, dim3((unsigned)n), dim3(64), 0, stream, out);
   return hipGetLastError();
 }
 

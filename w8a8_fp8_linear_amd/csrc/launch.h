@@ -33,6 +33,7 @@ hipError_t launch_quant_gemm_decode(const uint16_t* x, const uint8_t* w, const f
 // workgroup; sink gets one XOR word per workgroup.
 constexpr int64_t kProbeBytesPerBlock = 32768;
 hipError_t launch_read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_clock_probe(uint64_t* out, int64_t n, hipStream_t stream);
 
 // Default maths (w8a16.hip): y[m,n] = bf16(sw[n] * sum_k x[m,k] w[n,k]), x BF16,
 // w E4M3 widened to BF16, BF16 MFMA.
