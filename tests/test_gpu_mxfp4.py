@@ -36,7 +36,7 @@ import w8a8_fp8_linear_amd as w8  # noqa: E402
 
 SMALL = dict(T=37, H=256, I=256, E=5, k=3, n_outlier=2)
 RAGGED = dict(T=301, H=384, I=384, E=9, k=4, n_outlier=3)   # a half K stage, 3 gate/up tiles, odd groups
-MID = dict(T=500, H=384, I=384, E=4, k=2, n_outlier=3)       # 250 rows per group: the 128 x 128 tiles
+MID = dict(T=960, H=384, I=384, E=4, k=2, n_outlier=3)       # 480 rows per group: the 128 x 128 tiles
 PRAXIS = dict(T=4096, H=1024, I=512, E=128, k=4, n_outlier=10, passes=2)
 
 
