@@ -578,17 +578,18 @@ __global__ __launch_bounds__(256) void combine_mx(const float* __restrict__ y, c
   }
 }
 
-// Tile shapes: 256 x 256 tiles of 8 waves from 512 rows per group on
-// average; 128 x 128 tiles of 2 x 2 waves from 448 to 511 rows; 64 x 128 tiles
-// of 1 x 2 waves below 448. Both small shapes take one LDS stage at three
+// Tile shapes: 256 x 256 tiles of 8 waves from 1024 rows per group on
+// average; 128 x 128 tiles of 2 x 2 waves from 448 to 1023 rows; 64 x 128
+// tiles of 1 x 2 waves below 448. Both small shapes take one LDS stage at three
 // waves per SIMD: the 64 x 128 tiles need 26 KB instead of 52 KB and 78-82
 // VGPRs, so six workgroups fit on a CU instead of three (16-19% less time
 // for a whole two-pass FFN at 128 and 192 experts); the 128 x 128 tiles 36 KB
 // instead of 70 KB and 75-80 VGPRs, three workgroups instead of two. With
 // both in one stage the 64 x 128 tiles were 2-5% faster than the 128 x 128
 // ones up to 384 rows per group (the FP8 tiles cross over near 256 rows and
-// keep their threshold). The same results bit for bit.
-constexpr int64_t kMxSmallGroupRows = 512, kMxTinyGroupRows = 448;
+// keep their threshold), and the 128 x 128 tiles beat the 256 x 256 ones at
+// 512 and 768 rows (5% and 1.4%). The same results bit for bit.
+constexpr int64_t kMxSmallGroupRows = 1024, kMxTinyGroupRows = 448;
 
 template <int BM, int BN, int WGM, int WGN, int MODE, int OCC, int NS = 2>
 hipError_t run_mx(MxArgs a, int64_t max_rows, hipStream_t stream) {
