@@ -209,6 +209,15 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
     # from a HIP graph instead.
     q_ms, _ = _per_launch_ms([lambda: w8.quantize_per_token(x, xq, xs)] * 40, 5, stream)
     q_avg = sum(q_ms) / len(q_ms)
+    # Back to back, each XCD re-reads the rows it read one launch earlier from
+    # its own L2. Inside a step the GEMM has replaced them, so the quantiser
+    # reads from memory: what it adds to a step is the time of 20 steps less
+    # that of 20 GEMMs alone (HIP-graph replays, alternated, medians).
+    pair_ms, solo_ms = [], []
+    for _ in range(2):
+        pair_ms += _per_launch_ms([step] * 20, 5, stream)[0]
+        solo_ms += _per_launch_ms([lambda: w8.w8a8_gemm(xq, xs, wq, ws, out=y)] * 20, 5, stream)[0]
+    q_in_step = sorted(pair_ms)[len(pair_ms) // 2] - sorted(solo_ms)[len(solo_ms) // 2]
 
     import numpy as np
 
@@ -235,6 +244,7 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
         "settle_clock": clock,
         "gemm_tflops": flops / (gemm_avg * 1e-3) / 1e12, "gemm_flops": flops, "gemm_bytes": gemm_bytes,
         "quant_ms_avg": q_avg, "quant_gbs": q_bytes / (q_avg * 1e-3) / 1e9, "quant_bytes": q_bytes,
+        "quant_ms_in_step": q_in_step, "quant_gbs_in_step": q_bytes / (q_in_step * 1e-3) / 1e9,
         "tokens_per_s": M * steps / wall, "y_bits": y_bits,
     }
 
@@ -960,6 +970,12 @@ def main():
                                  "workgroups) read right after it on the same stream"},
         "quant_us_avg": round(pre["quant_ms_avg"] * 1e3, 3),
         "quant_GBs": round(pre["quant_gbs"], 1),
+        "quant_us_in_step": round(pre["quant_ms_in_step"] * 1e3, 3),
+        "quant_GBs_in_step": round(pre["quant_gbs_in_step"], 1),
+        "quant_timing": ("quant_us_avg: 40 back-to-back launches from a HIP graph, where each XCD finds the rows it "
+                         "quantised one launch earlier in its L2; quant_us_in_step: 20 graph-replayed steps "
+                         "(quantiser + GEMM) less 20 GEMMs alone, medians: the quantiser reading its input from "
+                         "memory after a GEMM, as in the timed steps"),
         "tokens_per_s": round(pre["tokens_per_s"], 1),
         "decode": dec,
         "decode_layer_fast_math": dec_layer,
