@@ -139,6 +139,10 @@ GEMM_SHAPES = [
     # last workgroup's second tile past N; K = 272 / 2064 end inside a 128-deep step
     ("ragged_24x1040x272", 24, 1040, 272),
     ("ragged_32x48x2064", 32, 48, 2064),
+    # 5..16 rows (two weight tiles per workgroup, inputs straight into registers) and 2..4 rows
+    # (one tile per workgroup), both with K ending inside a step
+    ("ragged_12x1040x272", 12, 1040, 272),
+    ("ragged_3x48x2064", 3, 48, 2064),
 ]
 
 
