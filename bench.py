@@ -120,17 +120,14 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
     # right after it (clock_probe, 4 us per step), which shows the throttle.
     kClockSteps = 400
     clk = torch.empty((kClockSteps, 256, 2), dtype=torch.int64, device="cuda")
-    clk_evs = _events(kClockSteps)
+    clk_evs = _kernel_events(kClockSteps, stream)
     settled = 0
     t_end = time.perf_counter() + settle_ms * 1e-3
     while time.perf_counter() < t_end or settled < kClockSteps:
         for _ in range(10):
             if settled < kClockSteps:
-                a, b = clk_evs[settled]
                 w8.quantize_per_token(x, xq, xs)
-                a.record(stream)
-                w8.w8a8_gemm(xq, xs, wq, ws, out=y)
-                b.record(stream)
+                w8.w8a8_gemm(xq, xs, wq, ws, out=y, events=clk_evs[settled])
                 w8.clock_probe(256, clk[settled])
             else:
                 step()
@@ -146,20 +143,19 @@ def bench_prefill(steps, warmup, settle_ms=30.0):
     # rate can bound this), and captured once into a HIP graph and replayed
     # (every launch of the hot path, nothing skipped; a replayed graph adds
     # its own per-node cost on some hosts). The faster of the two is the
-    # step time; both are reported. In the eager runs each GEMM launch is
-    # bracketed by HIP events on its stream: their average is the roofline
-    # kernel's launch duration over the timed region.
+    # step time; both are reported. In the eager runs each GEMM is launched
+    # with a pair of HIP events that the runtime stamps with the kernel's own
+    # start and end (w8a8_gemm_timed): their average is the roofline kernel's
+    # launch duration over the timed region.
     wall_eager = None
     gemm_evs = []
     for _ in range(3):
-        evs = _events(steps)
+        evs = _kernel_events(steps, stream)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for a, b in evs:
+        for ev in evs:
             w8.quantize_per_token(x, xq, xs)
-            a.record(stream)
-            w8.w8a8_gemm(xq, xs, wq, ws, out=y)
-            b.record(stream)
+            w8.w8a8_gemm(xq, xs, wq, ws, out=y, events=ev)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         wall_eager = dt if wall_eager is None else min(wall_eager, dt)
@@ -462,6 +458,21 @@ def _events(n):
     import torch
 
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def _kernel_events(n, stream):
+    """n event pairs for w8a8_gemm's `events` argument, each recorded once
+    here so that the HIP events exist before a timed region (torch creates an
+    event on its first record); the launch then stamps them with the
+    kernel's own start and end."""
+    import torch
+
+    evs = _events(n)
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return evs
 
 
 def _avg_ms(evs):
@@ -957,15 +968,16 @@ def main():
                                      else round(pre["ms_per_step_graph"], 5)),
         "library_reference": pre["library_reference"],
         "gemm_us_avg": round(pre["gemm_ms_avg"] * 1e3, 3),
-        "gemm_us_timing": (f"HIP events around each of the {pre['gemm_launches_timed']} GEMM launches of the "
-                           "timed eager steps; each pair also spans the GEMM's dispatch behind the quantiser"),
+        "gemm_us_timing": (f"HIP events stamped with the kernel's own start and end (hipExtLaunchKernel, "
+                           f"w8a8_gemm_timed) on each of the {pre['gemm_launches_timed']} GEMM launches of the "
+                           "timed eager steps, on the launch stream"),
         "gemm_us_min_median_max": [round(pre["gemm_ms_min"] * 1e3, 3), round(pre["gemm_ms_median"] * 1e3, 3),
                                    round(pre["gemm_ms_max"] * 1e3, 3)],
         "gemm_us_back_to_back_launches": round(pre["gemm_ms_back_to_back"] * 1e3, 3),
         "settle": {"ms": pre["settle_ms"], "steps": pre["settle_steps"],
                    "what": "untimed back-to-back steps before the warm-up steps (power-controller transient)",
                    "clock_by_launch": pre["settle_clock"],
-                   "clock_what": "the first 400 settle steps: each GEMM timed with HIP events, then clock_probe "
+                   "clock_what": "the first 400 settle steps: each GEMM timed with kernel-stamped HIP events, then clock_probe "
                                  "(shader cycles over 4 us of the 100 MHz clock, median of 256 one-wave "
                                  "workgroups) read right after it on the same stream"},
         "quant_us_avg": round(pre["quant_ms_avg"] * 1e3, 3),

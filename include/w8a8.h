@@ -114,6 +114,25 @@ int quantize_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, uint8_t* q_
 int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
               uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * w8a8_gemm_timed — w8a8_gemm whose kernel the runtime times, for measurement.
+ *
+ * The same checks, kernels and result bits as w8a8_gemm. The kernel is
+ * launched with hipExtLaunchKernel, which records `start` when the kernel
+ * begins and `stop` when it ends, so hipEventElapsedTime(start, stop) is the
+ * kernel's own duration, without the dispatch that precedes it on the
+ * stream. This is how the throughput comparison of the fast-math layer is
+ * measured here (Lernex/Metis-1.6-Logos-FP8, "What --fast-math does").
+ *
+ *   start, stop  caller-created events (hipEventCreate, timing enabled);
+ *                neither may be NULL. When M == 0 or N == 0 no kernel runs
+ *                and the events are not recorded.
+ * Errors: those of w8a8_gemm; NULL_ARG also for a NULL event.
+ */
+int w8a8_gemm_timed(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
+                    uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream, hipEvent_t start,
+                    hipEvent_t stop);
+
 
 /*
  * e4m3_from_f32, bf16_from_f32 — the final conversions of this library on

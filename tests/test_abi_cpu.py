@@ -75,6 +75,18 @@ def test_gemm_argument_errors():
     assert f(P, P, P + 1, P, P, 4, 16, 16, None) == MIS
 
 
+def test_gemm_timed_argument_errors():
+    f = w8.lib().w8a8_gemm_timed
+    E = ctypes.c_void_p(64)  # a non-null event handle; never used on these paths
+    assert f(P, P, P, P, P, 4, 16, 16, None, None, E) == NULL
+    assert f(P, P, P, P, P, 4, 16, 16, None, E, None) == NULL
+    assert f(P, P, P, P, P, -1, 16, 16, None, E, E) == SHAPE
+    assert f(P, P, P, P, P, 4, 16, 8, None, E, E) == UNSUP
+    assert f(P, P, P, P, P, 0, 16, 16, None, E, E) == OK
+    assert f(None, P, P, P, P, 4, 16, 16, None, E, E) == NULL
+    assert f(P, P, P + 1, P, P, 4, 16, 16, None, E, E) == MIS
+
+
 def test_valid_call_without_gpu_reports_device():
     import torch
     if torch.cuda.is_available():

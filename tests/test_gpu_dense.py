@@ -226,6 +226,35 @@ def test_gemm_invariants():
     assert rep["n_bound_violations"] == 0
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 6144, 2048), (300, 512, 1024), (8, 8192, 2048), (32, 8192, 2048), (3, 48, 64)])
+def test_gemm_timed_same_bits(M, N, K):
+    """w8a8_gemm_timed: the same kernels and bits as w8a8_gemm (tiled and
+    every decode variant), and its events span a positive time no longer than
+    the host's own clock around the call."""
+    import time
+
+    print(f"[gemm timed] M={M} N={N} K={K}", flush=True)
+    d = synth.dense_workload(M=M, K=K, N=N, n_outlier=max(1, K // 100), seed=11)
+    qx, sx, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["x"]))
+    qw, sw, _ = oracle.quantize_rows(synth.bf16_bits_to_f32(d["w"]))
+    base = _run_gemm(qx, sx, qw, sw)
+    a, sa, w, ws = to_dev(qx), to_dev(sx), to_dev(qw), to_dev(sw)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):  # the second call reuses the events created by the first
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        w8.w8a8_gemm(a, sa, w, ws, out=y, events=(e0, e1))
+        torch.cuda.synchronize()
+        wall_ms = 1e3 * (time.perf_counter() - t0)
+        assert np.array_equal(bf16_bits(y), base), "timed launch differs from w8a8_gemm"
+        ms = e0.elapsed_time(e1)
+        assert 0.0 < ms <= wall_ms, (ms, wall_ms)
+        y.fill_(float("nan"))
+    with pytest.raises(TypeError):
+        w8.w8a8_gemm(a, sa, w, ws, events=(None, None))
+
+
 def test_gemm_empty():
     a = torch.empty((0, 32), dtype=torch.uint8, device="cuda")
     s = torch.empty((0,), dtype=torch.float32, device="cuda")

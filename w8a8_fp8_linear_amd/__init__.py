@@ -35,6 +35,8 @@ _SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quantize_per_token": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "w8a8_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
+    "w8a8_gemm_timed": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr,
+                                       _c_ptr, _c_ptr]),
     "w8a16_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
     "fp8_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "fp8_linear_single_launch": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr]),
@@ -166,8 +168,12 @@ def quantize_per_token(x, q=None, scale=None):
     return q, scale
 
 
-def w8a8_gemm(a_q, a_scale, w_q, w_scale, out=None):
-    """y[m, n] = bf16(a_scale[m] * w_scale[n] * sum_k a_q[m, k] * w_q[n, k]) (E4M3 operands)."""
+def w8a8_gemm(a_q, a_scale, w_q, w_scale, out=None, events=None):
+    """y[m, n] = bf16(a_scale[m] * w_scale[n] * sum_k a_q[m, k] * w_q[n, k]) (E4M3 operands).
+
+    events: optional (start, stop) pair of timing torch.cuda.Event; the
+    kernel is then launched through w8a8_gemm_timed, which stamps them with
+    its own start and end (start.elapsed_time(stop) is the kernel alone)."""
     import torch
 
     _want(a_q, torch.uint8, 2, "a_q")
@@ -183,8 +189,20 @@ def w8a8_gemm(a_q, a_scale, w_q, w_scale, out=None):
     _want(out, torch.bfloat16, 2, "out")
     if tuple(out.shape) != (M, N):
         raise ValueError("out must be [M, N]")
-    _check("w8a8_gemm", lib().w8a8_gemm(a_q.data_ptr(), a_scale.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(),
-                                        out.data_ptr(), M, N, K, _stream(a_q)))
+    if events is None:
+        _check("w8a8_gemm", lib().w8a8_gemm(a_q.data_ptr(), a_scale.data_ptr(), w_q.data_ptr(),
+                                            w_scale.data_ptr(), out.data_ptr(), M, N, K, _stream(a_q)))
+        return out
+    start, stop = events
+    stream = torch.cuda.current_stream(a_q.device)
+    for ev in (start, stop):
+        if not isinstance(ev, torch.cuda.Event):
+            raise TypeError("events must be torch.cuda.Event objects")
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record(stream)
+    _check("w8a8_gemm_timed", lib().w8a8_gemm_timed(a_q.data_ptr(), a_scale.data_ptr(), w_q.data_ptr(),
+                                                    w_scale.data_ptr(), out.data_ptr(), M, N, K, stream.cuda_stream,
+                                                    start.cuda_event, stop.cuda_event))
     return out
 
 

@@ -98,8 +98,9 @@ int quantize_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, uint8_t* q_
   return launch_status(w8a8::launch_quantize_rows(x_bf16, M, K, q_e4m3, scale, stream));
 }
 
-int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
-              uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+static int gemm_checked(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
+                        uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
   if (M < 0 || N < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N) || !mul_ok(M * N, 2))
     return W8A8_ERR_BAD_SHAPE;
   if (K == 0 || K % 16 != 0 || K > (int64_t(1) << 20)) return W8A8_ERR_UNSUPPORTED;
@@ -110,7 +111,19 @@ int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, cons
     return W8A8_ERR_MISALIGNED;
   const int d = check_device();
   if (d != W8A8_OK) return d;
-  return launch_status(w8a8::launch_gemm(a_q, a_scale, w_q, w_scale, y_bf16, M, N, K, stream));
+  return launch_status(w8a8::launch_gemm(a_q, a_scale, w_q, w_scale, y_bf16, M, N, K, stream, start, stop));
+}
+
+int w8a8_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
+              uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  return gemm_checked(a_q, a_scale, w_q, w_scale, y_bf16, M, N, K, stream, nullptr, nullptr);
+}
+
+int w8a8_gemm_timed(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q, const float* w_scale,
+                    uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream, hipEvent_t start,
+                    hipEvent_t stop) {
+  if (!start || !stop) return W8A8_ERR_NULL_ARG;
+  return gemm_checked(a_q, a_scale, w_q, w_scale, y_bf16, M, N, K, stream, start, stop);
 }
 
 int w8a16_gemm(const uint16_t* x_bf16, const uint8_t* w_q, const float* w_scale, uint16_t* y_bf16, int64_t M,

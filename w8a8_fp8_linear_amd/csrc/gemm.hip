@@ -40,6 +40,8 @@
 // Within one 128-byte K slice, lane group g (lane / 16) of an MFMA operand
 // holds the 16-byte chunks g and g + 4 of its row. A and W use the same
 // assignment, so the product is the full dot product over the slice.
+#include <hip/hip_ext.h>
+
 #include "device.h"
 #include "launch.h"
 
@@ -499,43 +501,52 @@ __global__ __launch_bounds__(64) void clock_probe(uint64_t* __restrict__ out) {
   out[2 * blockIdx.x + 1] = (uint64_t)(r1 - r0);
 }
 
+// A launch, optionally with two events that the runtime stamps with the
+// kernel's own start and end (hipExtLaunchKernel), so that an elapsed time
+// between them is the kernel alone, without the dispatch in front of it.
+template <typename F, typename... Args>
+hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                    Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t run_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
-                     int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                     int64_t M, int64_t N, int64_t K, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tiled<BM, BN, WGM, WGN>), dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0, stream, a,
-                     sa, w, sw, y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
-  return hipGetLastError();
+  return launch_k(gemm_tiled<BM, BN, WGM, WGN>, dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), stream, start, stop,
+                  a, sa, w, sw, y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (M == 0 || N == 0) return hipSuccess;
   // Up to 4 rows one 16-row weight tile per workgroup keeps the most bytes
   // in flight; from 5 rows two tiles per workgroup share each input
   // fragment, halving the input rows read per weight byte (8 rows of an
   // 8192 x 2048 layer: 5.62 against 5.75 us; 1 row: 5.26 against 5.47 us).
   if (M <= 4) {
-    hipLaunchKernelGGL((gemm_skinny<1, 4>), dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, a, sa, w, sw,
-                       y, (int)M, (int)N, (int)K);
-    return hipGetLastError();
+    return launch_k(gemm_skinny<1, 4>, dim3((unsigned)((N + 15) / 16)), dim3(256), stream, start, stop, a, sa, w, sw, y,
+                    (int)M, (int)N, (int)K);
   }
   if (M <= 16) {
-    hipLaunchKernelGGL((gemm_skinny<1, 4, 2>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, stream, a, sa, w, sw,
-                       y, (int)M, (int)N, (int)K);
-    return hipGetLastError();
+    return launch_k(gemm_skinny<1, 4, 2>, dim3((unsigned)((N + 31) / 32)), dim3(256), stream, start, stop, a, sa, w, sw, y,
+                    (int)M, (int)N, (int)K);
   }
   // 17 to 32 rows: the input rows go through LDS as whole 128-byte row
   // pieces (7.2 -> 6.6 us for 32 rows of the 8192 x 2048 layer; at 8 to 16
   // rows the extra LDS hop costs as much as it saves)
   if (M <= 32) {
-    hipLaunchKernelGGL((gemm_skinny<2, 4, 2, true>), dim3((unsigned)((N + 31) / 32)), dim3(256), 0, stream, a, sa, w, sw,
-                       y, (int)M, (int)N, (int)K);
-    return hipGetLastError();
+    return launch_k(gemm_skinny<2, 4, 2, true>, dim3((unsigned)((N + 31) / 32)), dim3(256), stream, start, stop, a, sa, w, sw, y,
+                    (int)M, (int)N, (int)K);
   }
-  return run_tiled<256, 192, 2, 4>(a, sa, w, sw, y, M, N, K, stream);
+  return run_tiled<256, 192, 2, 4>(a, sa, w, sw, y, M, N, K, stream, start, stop);
 }
 
 hipError_t launch_read_probe(const uint8_t* p, int64_t bytes, uint32_t* sink, hipStream_t stream) {

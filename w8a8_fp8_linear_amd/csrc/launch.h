@@ -18,8 +18,10 @@ hipError_t launch_convert_e4m3(const float* v, int64_t n, uint8_t* q, hipStream_
 hipError_t launch_convert_bf16(const float* v, int64_t n, uint16_t* y, hipStream_t stream);
 
 // Dense scaled FP8 GEMM: y[m,n] = bf16(sa[m] * sw[n] * sum_k a[m,k] w[n,k]).
+// start / stop: optional events stamped with the kernel's own start and end
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
-                       uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                       uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                       hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Per-token quantisation fused into the decode GEMM (one launch), for
 // M <= kFusedDecodeMaxM and K <= kFusedDecodeMaxK; bit-identical to
