@@ -124,6 +124,21 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // The epilogue's scales are loaded before the K loop, so that their
+  // latency passes under it instead of following the last MFMAs.
+  float sA[C::SM];
+  float4 sWv[C::SN];
+#pragma unroll
+  for (int j = 0; j < C::SM; ++j) {
+    const int m = m0 + wm * C::WM + j * 16 + r16;
+    sA[j] = m < M ? sa[m] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < C::SN; ++i) {
+    const int nl = wn * C::WN + i * 16 + 4 * g;
+    sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(sw + n0 + nl) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
   const int nk = (K + 127) >> 7;
   v8i xf[C::SM], wf[C::SN];
   if (loader) {
@@ -155,19 +170,6 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
 
   // Epilogue. acc[i][j][r] is Y[m][n] with m = m-tile j, lane % 16 and
   // n = n-tile i, 4 * (lane / 16) + r: four consecutive outputs of one row.
-  // all scale loads are issued before the barrier, and waited for together
-  float sA[C::SM];
-  float4 sWv[C::SN];
-#pragma unroll
-  for (int j = 0; j < C::SM; ++j) {
-    const int m = m0 + wm * C::WM + j * 16 + r16;
-    sA[j] = m < M ? sa[m] : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < C::SN; ++i) {
-    const int nl = wn * C::WN + i * 16 + 4 * g;
-    sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(sw + n0 + nl) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < C::SN; ++i) {
