@@ -385,6 +385,27 @@ void grouped_tiled(const GroupedArgs p) {
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int nk = (K + 127) >> 7;
+  // The epilogue's weight-row scales (per lane: four consecutive columns of
+  // each of its SN column blocks; for GATE_UP_H block i holds gate columns
+  // when i is even and the matching up columns when i is odd). The large
+  // tiles (two waves per SIMD, registers to spare) load them before the K
+  // loop, so that their latency passes under it; the small tiles, at three
+  // waves per SIMD, load them after it.
+  float4 esc[C::SN];
+  auto load_scales = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::SN; ++i) {
+      if (MODE == kGateUpH) {
+        const int hc = (n0 >> 1) + (((wn * C::WN + (i & ~1) * 16) >> 5) << 4) + 4 * g;
+        esc[i] = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + (i & 1 ? N / 2 : 0) + hc);
+      } else {
+        const int n = n0 + wn * C::WN + i * 16 + 4 * g;
+        esc[i] = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  constexpr bool kScalesFirst = OCC <= 2;
+  if (kScalesFirst) load_scales();
   issue(0, 0);
   if (kIsDown) {
     setup_rows();
@@ -441,12 +462,8 @@ void grouped_tiled(const GroupedArgs p) {
     constexpr int kJH = C::kJH, kPartRows = C::WM / kJH, kPartJ = C::SM / kJH;
     static_assert(kPartRows * BN * 4 <= C::kLds && C::SM % kJH == 0, "a part of a wm's rows must fit in the LDS");
     static_assert(kChunks >= 16 && 64 % kChunks == 0, "row pieces must tile a wave");
-    float4 sW[C::SN];
-#pragma unroll
-    for (int i = 0; i < C::SN; ++i) {
-      const int n = n0 + wn * C::WN + i * 16 + 4 * g;
-      sW[i] = n < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    if (!kScalesFirst) load_scales();
+    const float4* const sW = esc;
 #pragma unroll
     for (int pass = 0; pass < WGM * kJH; ++pass) {
       const int pw = pass / kJH, ph = pass % kJH;
@@ -491,18 +508,12 @@ void grouped_tiled(const GroupedArgs p) {
       rs[j] = row_scale[ml];
       amax[j] = 0.f;
     }
-    float4 gsv[C::SN / 2], usv[C::SN / 2];  // gate and up scales, loaded together
-#pragma unroll
-    for (int i = 0; i < C::SN; i += 2) {
-      const int hc = (n0 >> 1) + (((wn * C::WN + i * 16) >> 5) << 4) + 4 * g;
-      gsv[i / 2] = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + hc);
-      usv[i / 2] = *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + Ih + hc);
-    }
+    if (!kScalesFirst) load_scales();  // gate and up scales, loaded together
 #pragma unroll
     for (int i = 0; i < C::SN; i += 2) {  // i: gate block, i + 1: its up block
       const int sr = wn * C::WN + i * 16;
       const int hc = (n0 >> 1) + ((sr >> 5) << 4) + 4 * g;  // h column of this lane's first value
-      const float4 gs4 = gsv[i / 2], us4 = usv[i / 2];
+      const float4 gs4 = esc[i], us4 = esc[i + 1];
       const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w}, us[4] = {us4.x, us4.y, us4.z, us4.w};
 #pragma unroll
       for (int j = 0; j < C::SM; ++j) {
@@ -530,18 +541,12 @@ void grouped_tiled(const GroupedArgs p) {
     return;
   }
   // GATE_UP: scale, round to BF16, stage in LDS, store full row segments
-  float4 sWv[C::SN];  // the weight scales, loaded together before the barrier
-#pragma unroll
-  for (int i = 0; i < C::SN; ++i) {
-    const int nl = wn * C::WN + i * 16 + 4 * g;
-    sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(p.sB + (int64_t)e * N + n0 + nl)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  if (!kScalesFirst) load_scales();  // the weight scales, loaded together before the barrier
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < C::SN; ++i) {
     const int nl = wn * C::WN + i * 16 + 4 * g;
-    const float4 sW = sWv[i];
+    const float4 sW = esc[i];
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;

@@ -133,6 +133,15 @@ void w8a16_tiled(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W, 
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // The epilogue's weight-row scales are loaded before the K loop, so that
+  // their latency passes under it.
+  float4 sWv[C::SN];
+#pragma unroll
+  for (int i = 0; i < C::SN; ++i) {
+    const int nl = wn * C::WN + i * 16 + 4 * g;
+    sWv[i] = n0 + nl < N ? *reinterpret_cast<const float4*>(sw + n0 + nl) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
   const int nk = (K + 63) >> 6;
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
@@ -167,8 +176,7 @@ void w8a16_tiled(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W, 
 #pragma unroll
   for (int i = 0; i < C::SN; ++i) {
     const int nl = wn * C::WN + i * 16 + 4 * g;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (n0 + nl < N) s = *reinterpret_cast<const float4*>(sw + n0 + nl);
+    const float4 s = sWv[i];
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) {
       const int ml = wm * C::WM + j * 16 + r16;
