@@ -446,15 +446,32 @@ void mx_grouped(const MxArgs p) {
         }
       }
       __syncthreads();
+      // The large tiles: all of a thread's LDS reads first, then its stores
+      // (one LDS latency). The small tiles, at three waves per SIMD, one
+      // piece at a time, to stay in their register budget.
       const int c = lane % kChunks;
       const int n = n0 + c * 4;
-      for (int rl = wave * kRowsPerInst + lane / kChunks; rl < kPartRows; rl += (C::kThreads / 64) * kRowsPerInst) {
-        const int ml = pw * C::WM + ph * kPartRows + rl;
-        const int slot = row_tok[ml];
-        const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot;
-        if (slot >= 0 && n < N)
-          store16_nt(p.out_f32 + yrow * N + n,
-                     *reinterpret_cast<const float4*>(smem + rl * (BN * 4) + ((c ^ (rl & 15)) << 4)));
+      constexpr int kStep = (C::kThreads / 64) * kRowsPerInst;
+      constexpr int kPieces = kPartRows / kStep;
+      constexpr int kBatch = OCC <= 2 ? kPieces : 1;
+      static_assert(kPartRows % kStep == 0 && kPieces % kBatch == 0, "the staged rows must split evenly");
+      const int rl0 = wave * kRowsPerInst + lane / kChunks;
+#pragma unroll 1
+      for (int b = 0; b < kPieces; b += kBatch) {
+        float4 piece[kBatch];
+        int slot[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const int rl = rl0 + (b + q) * kStep;
+          piece[q] = *reinterpret_cast<const float4*>(smem + rl * (BN * 4) + ((c ^ (rl & 15)) << 4));
+          slot[q] = row_tok[pw * C::WM + ph * kPartRows + rl];
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const int ml = pw * C::WM + ph * kPartRows + rl0 + (b + q) * kStep;
+          const int64_t yrow = p.slot_row != nullptr ? (int64_t)(row0 + ml) : (int64_t)slot[q];
+          if (slot[q] >= 0 && n < N) store16_nt(p.out_f32 + yrow * N + n, piece[q]);
+        }
       }
     }
     return;
