@@ -141,14 +141,22 @@ void gemm_tiled(const uint8_t* __restrict__ A, const float* __restrict__ sa,
 
   const int nk = (K + 127) >> 7;
   v8i xf[C::SM], wf[C::SN];
+  // The first two K steps are requested together, and only the first is
+  // waited for: the second one's latency then runs under the first step
+  // instead of after it.
   if (loader) {
     issue(0, 0);
-    wait_vmem_all();
+    if (nk > 1) {
+      issue(1, 128);
+      wait_vmcnt<C::kLoads>();
+    } else {
+      wait_vmem_all();
+    }
   }
   lds_barrier();
   if (!loader) lds_barrier();
   for (int kt = 0; kt < nk; ++kt) {
-    if (loader && kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
+    if (loader && kt >= 1 && kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) << 7);
     const uint8_t* st = smem + (kt & 1) * C::kStage;
 #pragma unroll
     for (int j = 0; j < C::SM; ++j) xf[j] = lds_frag(st, BN + wm * C::WM + j * 16 + r16, g);
