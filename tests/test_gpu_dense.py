@@ -139,6 +139,11 @@ GEMM_SHAPES = [
     # last workgroup's second tile past N; K = 272 / 2064 end inside a 128-deep step
     ("ragged_24x1040x272", 24, 1040, 272),
     ("ragged_32x48x2064", 32, 48, 2064),
+    # the tiled kernel with exactly two K steps (both requested before its loop, none in it),
+    # with the second one ragged, and with three (one requested in the loop)
+    ("two_steps_257x400x256", 257, 400, 256),
+    ("two_steps_ragged_70x208x144", 70, 208, 144),
+    ("three_steps_300x192x384", 300, 192, 384),
     # 5..16 rows (two weight tiles per workgroup, inputs straight into registers) and 2..4 rows
     # (one tile per workgroup), both with K ending inside a step
     ("ragged_12x1040x272", 12, 1040, 272),
